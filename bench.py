@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Benchmark of the capacity-padded, permute-free MoE FFN forward on one MI355X.
+
+One step = the whole forward (top-K routing + capacity selection, align,
+gather-in-GEMM FC1+SwiGLU, FC2, gather-combine) over one batch of seeded
+synthetic inputs already resident in HBM, replayed from one captured
+hipGraph.  Prints ONE JSON line on stdout; progress goes to stderr.
+
+Timed regions (all on the stream the library launches on):
+  1. K graph replays between two HIP events -> ms_per_step, value.
+  2. K eager forwards with a HIP event between consecutive C-ABI calls ->
+     average duration of each call's kernels (route+capacity, align, FC1,
+     FC2, combine) -> TFLOP/s, GB/s and the roofline of the dominant kernel
+     (FC1).
+  3. cpu_baseline: the CPU oracle on the same inputs (median of a few full
+     forwards), rank 0 only.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "routed tokens/s + grouped-GEMM TFLOP/s (% bf16 MFMA peak), MoE FFN fwd, 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_fc1_swiglu_qwen3_30b_a3b.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    """Hash of the FFN kernel source: counter summaries taken on other code are void."""
+    p = os.path.join(ROOT, "mixture_experts_expert_amd", "csrc", "grouped_ffn.hip")
+    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+
+
+def algorithmic_bytes(w, C, Cp, kept):
+    """Bytes each call must move at least once (read + write), per forward."""
+    N, H, I, E, K = w.N, w.H, w.I, w.E, w.K
+    R = E * Cp
+    return {
+        "route_capacity": N * E * 4 + N * K * (4 + 4) + N * K * (4 + 4) + N * K * 4 + E * 4,
+        "align": N * K * 12 + E * 4 + R * 8 + (R // 32) * 4 + E * 4 + N * K * 4 + N * 4 + 4,
+        "fc1": E * 2 * I * H * 2 + N * H * 2 + R * 8 + R * I * 2,
+        "fc2": E * H * I * 2 + R * I * 2 + R * H * 2,
+        "combine": kept * H * 2 + N * K * 4 + N * H * 2,
+    }
+
+
+def pmc_traffic(launch_bytes_unit):
+    """FC1's HBM traffic per launch from the committed rocprofv3 counter summary,
+    scaled by the copy-kernel calibration; None if absent or taken on other code."""
+    try:
+        d = json.load(open(PMC_SUMMARY))
+    except (OSError, ValueError):
+        return None
+    if d.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return int(d["fetch_bytes_per_launch"] * d["fetch_scale"] + d["write_bytes_per_launch"] * d["write_scale"])
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the FETCH/WRITE counters."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+def cpu_baseline(T, w, forwards):
+    import numpy as np
+    import moe_inputs
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+        blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info() if p.get("user_api") == "blas"}))
+    except Exception:  # threadpoolctl missing: report the affinity set
+        threads, blas = len(os.sched_getaffinity(0)), "unknown"
+    lg = T["logits"].cpu().numpy()
+    x = moe_inputs.bf16_bits(T["x"])
+    w1 = moe_inputs.bf16_bits(T["w1"])
+    w2 = moe_inputs.bf16_bits(T["w2"])
+    times = []
+    for i in range(forwards):
+        t0 = time.perf_counter()
+        oracle.forward(lg, x, w1, w2, w.K, w.F)
+        times.append(time.perf_counter() - t0)
+        log(f"  oracle forward {i + 1}/{forwards}: {times[-1]:.2f} s")
+    med = statistics.median(times)
+    return {"value": w.N / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{forwards} full forwards of the {w.name} workload (median {med:.2f} s), "
+                      f"numpy float64 with {blas} BLAS"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the Qwen3-30B-A3B-shaped layer)")
+    ap.add_argument("--cpu-forwards", type=int, default=3, help="oracle forwards timed for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU MoE FFN forward only; runs on more than one GPU "
+              "are not part of this build (see DESIGN.md, 'Sharding')", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_inputs
+    import mixture_experts_expert_amd as moe
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return
+
+    w = moe_inputs.WORKLOADS[args.workload or moe_inputs.HEADLINE]
+    if w.skew:
+        raise SystemExit("skewed workloads are parity cases, not bench lines")
+    log(f"[bench] {w.name}: N={w.N} H={w.H} E={w.E} K={w.K} F={w.F} I={w.I}")
+    T = moe_inputs.make_tensors(w, "cuda")
+    buf = moe.MoEBuffers(w.N, w.H, w.I, w.E, w.K, w.F, "cuda")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def fwd():
+        buf.route_capacity(T["logits"])
+        buf.align()
+        buf.fc1_swiglu(T["x"], T["w1"])
+        buf.fc2(T["w2"])
+        buf.combine()
+
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            fwd()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        fwd()
+    torch.cuda.synchronize()
+
+    # ---- timed region 1: graph replays
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            graph.replay()
+        stream.synchronize()
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        ev1.record(stream)
+        stream.synchronize()
+        wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] graph replay: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
+
+    # ---- timed region 2: eager, one HIP event between consecutive calls
+    names = ["route_capacity", "align", "fc1", "fc2", "combine"]
+    calls = [lambda: buf.route_capacity(T["logits"]), buf.align,
+             lambda: buf.fc1_swiglu(T["x"], T["w1"]), lambda: buf.fc2(T["w2"]), buf.combine]
+    tot = {n: 0.0 for n in names}
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            fwd()
+        stream.synchronize()
+        for _ in range(args.steps):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+            evs[0].record(stream)
+            for i, c in enumerate(calls):
+                c()
+                evs[i + 1].record(stream)
+            stream.synchronize()
+            for i, n in enumerate(names):
+                tot[n] += evs[i].elapsed_time(evs[i + 1])
+    us = {n: tot[n] / args.steps * 1e3 for n in names}
+    log("[bench] eager per-call us: " + ", ".join(f"{n} {us[n]:.1f}" for n in names))
+
+    kept = int((buf.token_routes >= 0).sum().item())
+    nbytes = algorithmic_bytes(w, buf.C, buf.Cp, kept)
+    fc1_flops = 2.0 * w.E * buf.Cp * (2 * w.I) * w.H
+    fc2_flops = 2.0 * w.E * buf.Cp * w.H * w.I
+    gemm_tflops = (fc1_flops + fc2_flops) / ((us["fc1"] + us["fc2"]) * 1e-6) / 1e12
+    fc1_tflops = fc1_flops / (us["fc1"] * 1e-6) / 1e12
+    gbs = {n: nbytes[n] / (us[n] * 1e-6) / 1e9 for n in names}
+    traffic = pmc_traffic(nbytes["fc1"])
+
+    rec = {
+        "metric": METRIC,
+        "value": w.N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "N": w.N, "H": w.H, "E": w.E, "K": w.K, "F": w.F, "I": w.I,
+                   "C": buf.C, "Cp": buf.Cp, "timed": "hipGraph replay of the whole forward"},
+        "routes_per_s": w.N * w.K / (ms_per_step * 1e-3),
+        "gemm_tflops": gemm_tflops,
+        "gemm_frac_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+        "kernel_us": us,
+        "kernel_gbs": gbs,
+        "kernel_frac_hbm_peak": {n: gbs[n] / PEAK_HBM_GBS for n in names},
+        "kept_routes": kept,
+        "roofline": {"kernel": "fc1_swiglu (gather-in-GEMM FC1 + SwiGLU*prob)",
+                     "bound": "mfma", "achieved": fc1_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": fc1_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic,
+                     "algorithmic_bytes": nbytes["fc1"], "flops": fc1_flops,
+                     "hbm_gbs": gbs["fc1"], "hbm_frac": gbs["fc1"] / PEAK_HBM_GBS},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu_baseline: timing the oracle")
+        rec["cpu_baseline"] = cpu_baseline(T, w, args.cpu_forwards)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()

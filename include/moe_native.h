@@ -1,0 +1,165 @@
+/*
+ * moe_native.h -- C ABI of the capacity-padded, permute-free MoE FFN forward
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The forward runs in four calls, in this order, on one HIP stream:
+ *
+ *   moe_route_capacity   top-K softmax routing + fixed-capacity slot selection
+ *   moe_align            expert-sorted, block-padded route list and its inverse
+ *   moe_grouped_ffn_fwd  gather-in-GEMM FC1 -> SwiGLU*prob -> FC2 (bf16 MFMA)
+ *   moe_gather_combine   each token sums its own kept, already-weighted routes
+ *
+ * Pages defining the operations (cited by title and section):
+ *   [FC] "feat(cuda-graphs): capture fixed-capacity MoE execution"
+ *        (NVIDIA-NeMo Automodel pull request 2932), Design notes.
+ *   [PF] "Permute-Free Grouped GEMM for MoE (bf16, gfx950)"
+ *        (ROCm TransformerEngine pull request 694), sections 2-6.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every tensor pointer is a DEVICE pointer, owned by the caller, row-major
+ *   and contiguous, 16-byte aligned (MOE_ERR_MISALIGNED otherwise).  The
+ *   library keeps no pointer after a call returns.
+ * - bf16 tensors are passed as uint16_t bit patterns (IEEE bfloat16).
+ * - A call only enqueues kernels on `stream` (0 = the null stream).  It never
+ *   allocates, never synchronises and never reads device memory on the host,
+ *   so the four calls can be captured into one hipGraph and replayed.
+ * - Arguments are validated on the host from scalars only.  Anything outside
+ *   the supported envelope fails closed (no fallback path):
+ *       1 <= K <= min(E, 32),  1 <= E <= 1024,  0 <= N <= 16384,
+ *       H and I multiples of 64 in [64, 16384],
+ *       C = the value moe_source_capacity returns for (N, K, E, F).
+ *   N == 0 is a no-op that returns MOE_OK.
+ * - After launching, the call maps hipGetLastError() != hipSuccess to
+ *   MOE_ERR_LAUNCH.
+ * - The layout block BM is a library constant (moe_layout_block_m()); each
+ *   expert owns Cp = moe_padded_capacity(C) consecutive slots, and the route
+ *   list has R = E*Cp slots in total.
+ */
+#ifndef MOE_NATIVE_H
+#define MOE_NATIVE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,  /* null pointer, negative size, K > E, F <= 0, ... */
+    MOE_ERR_UNSUPPORTED = -2,  /* valid, but outside the supported envelope    */
+    MOE_ERR_MISALIGNED = -3,   /* a tensor pointer is not 16-byte aligned      */
+    MOE_ERR_LAUNCH = -4        /* a kernel launch reported an error            */
+} moe_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(int status);
+
+/* [FC] Design notes: source capacity C = ceil(N*K*F/E) slots per expert,
+ * evaluated exactly on the binary value of the double F (128-bit integer
+ * arithmetic, no float rounding decides the ceiling).
+ * Returns C >= 0, or MOE_ERR_INVALID_ARG (< 0) when N < 0, K < 1, E < 1,
+ * K > E, or F is not finite and positive; MOE_ERR_UNSUPPORTED when C would
+ * exceed 2^31 - 1.  Host-only, no device work. */
+int64_t moe_source_capacity(int64_t N, int32_t K, int32_t E, double F);
+
+/* Layout block BM: the number of slots in one route-list block ([PF]
+ * section 4, block_size_m).  Constant 32 (one 32x32 MFMA M-extent). */
+int32_t moe_layout_block_m(void);
+
+/* Per-expert segment length Cp = C rounded up to a multiple of BM
+ * (< 0 if C < 0).  Host-only. */
+int64_t moe_padded_capacity(int64_t C);
+
+/* Steps 1-2: top-K softmax routing and fixed-capacity drop-and-pad
+ * selection ([FC] Design notes; [PF] section 4, route_counts/route_within).
+ *
+ *   logits       in   float32 [N, E]  router logits
+ *   topk_ids     out  int32   [N, K]  chosen experts, descending logit;
+ *                                     equal logits -> lower expert first
+ *   topk_probs   out  float32 [N, K]  softmax over the K chosen logits:
+ *                                     float64 exp(l_k - l_0), summed in k
+ *                                     order, divided, rounded once to fp32
+ *   route_slot   out  int32   [N, K]  slot of route (t,k) inside its expert's
+ *                                     segment, or -1 if the route is dropped
+ *   expert_count out  int32   [E]     kept routes per expert = min(C, load)
+ *
+ * Per expert, the min(C, load) routes with the largest topk_probs are kept
+ * (equal probabilities: lower token first); kept routes take slots
+ * 0..count-1 in ascending token order. */
+int moe_route_capacity(const float* logits, int64_t N, int32_t E, int32_t K, int64_t C,
+                       int32_t* topk_ids, float* topk_probs, int32_t* route_slot,
+                       int32_t* expert_count, hipStream_t stream);
+
+/* Step 3: sync-free align ([PF] section 4, Data structures; section 5,
+ * route_list_align), fixed-capacity form: expert e owns slots
+ * [e*Cp, (e+1)*Cp).
+ *
+ *   topk_ids, topk_probs, route_slot [N, K], expert_count [E]   in (step 1-2)
+ *   sorted_slot_ids        out int32   [E*Cp]  slot -> token row to gather;
+ *                                              N (sentinel) for pad slots
+ *   slot_probs             out float32 [E*Cp]  routing probability; +0.0 at pads
+ *   expert_ids             out int32   [E*Cp/BM]  expert owning each block
+ *   block_start            out int32   [E]     first block of each expert
+ *   token_routes           out int32   [N, K]  slot of route (t,k), -1 if dropped
+ *   token_route_count      out int32   [N]     kept routes of each token
+ *   num_tokens_post_padded out int32   [1]     E*Cp, written as a device scalar
+ */
+int moe_align(const int32_t* topk_ids, const float* topk_probs, const int32_t* route_slot,
+              const int32_t* expert_count, int64_t N, int32_t E, int32_t K, int64_t C,
+              int32_t* sorted_slot_ids, float* slot_probs, int32_t* expert_ids,
+              int32_t* block_start, int32_t* token_routes, int32_t* token_route_count,
+              int32_t* num_tokens_post_padded, hipStream_t stream);
+
+/* Step 4: permute-free grouped FFN ([PF] sections 2-3 and 6).
+ *
+ *   x          in  bf16 [N, H]      token-order activations, never permuted
+ *   w1         in  bf16 [E, 2I, H]  FC1; rows 0..I-1 gate, rows I..2I-1 up
+ *   w2         in  bf16 [E, H, I]   FC2
+ *   sorted_slot_ids, slot_probs [E*Cp]   in (step 3)
+ *   act        out bf16 [E*Cp, I]   silu(x_r W1g^T) * (x_r W1u^T) * prob,
+ *                                   r = sorted_slot_ids[s]; a transient that
+ *                                   FC2 consumes
+ *   route_out  out bf16 [E*Cp, H]   act W2^T per slot (already weighted)
+ *
+ * FC1 gathers its A rows through sorted_slot_ids inside the tile loads (the
+ * sentinel row N reads as zeros); FC2 reads act by route position.  bf16
+ * MFMA with float32 accumulation; the SwiGLU and the probability are applied
+ * in FC1's epilogue.  Pad-slot rows of act and route_out come out as zeros. */
+int moe_grouped_ffn_fwd(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                        const int32_t* sorted_slot_ids, const float* slot_probs,
+                        int64_t N, int32_t H, int32_t I, int32_t E, int64_t C,
+                        uint16_t* act, uint16_t* route_out, hipStream_t stream);
+
+/* Step 4 as its two GEMM launches, for callers that schedule or time them
+ * separately ([PF] section 3: one align drives FC1 and FC2, a direction flag
+ * selects how A is read).  moe_grouped_ffn_fwd == moe_grouped_fc1_swiglu
+ * followed by moe_grouped_fc2 on the same stream, bit for bit.  Arguments,
+ * layouts and checks as in moe_grouped_ffn_fwd. */
+int moe_grouped_fc1_swiglu(const uint16_t* x, const uint16_t* w1, const int32_t* sorted_slot_ids,
+                           const float* slot_probs, int64_t N, int32_t H, int32_t I, int32_t E,
+                           int64_t C, uint16_t* act, hipStream_t stream);
+int moe_grouped_fc2(const uint16_t* act, const uint16_t* w2, int64_t N, int32_t H, int32_t I,
+                    int32_t E, int64_t C, uint16_t* route_out, hipStream_t stream);
+
+/* Step 5: contention-free gather-combine ([PF] sections 2 and 5,
+ * route_gather_combine): y[t] = bf16( float32 sum over k = 0..K-1 with
+ * token_routes[t,k] >= 0 of route_out[token_routes[t,k]] ), summed in k order
+ * from +0.0; no atomics, each output row has one writer.
+ *
+ *   route_out     in  bf16  [R, H] with R = E*Cp (rows indexed by slot)
+ *   token_routes  in  int32 [N, K]
+ *   y             out bf16  [N, H]
+ * R is needed to validate that no route index can fall outside route_out. */
+int moe_gather_combine(const uint16_t* route_out, const int32_t* token_routes, int64_t N,
+                       int32_t K, int32_t H, int64_t R, uint16_t* y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_NATIVE_H */

@@ -1,0 +1,25 @@
+"""MI355X-native capacity-padded, permute-free MoE FFN forward.
+
+The compute lives in libmoe_native.so (hand-written HIP for gfx950, C ABI in
+include/moe_native.h); this package is its thin ctypes binding plus a
+static-buffer forward helper.  Importing it fails loudly if the library is
+not built: there is no CPU or PyTorch fallback.
+"""
+
+from ._native import (  # noqa: F401
+    LIB_PATH,
+    MoEError,
+    header_functions,
+    lib,
+    moe_align,
+    moe_gather_combine,
+    moe_grouped_fc1_swiglu,
+    moe_grouped_fc2,
+    moe_grouped_ffn_fwd,
+    moe_layout_block_m,
+    moe_padded_capacity,
+    moe_route_capacity,
+    moe_source_capacity,
+    moe_status_string,
+)
+from .forward import MoEBuffers, forward  # noqa: F401

@@ -1,0 +1,188 @@
+"""ctypes binding of libmoe_native (the C ABI in include/moe_native.h).
+
+Argument marshalling only: every function takes torch tensors for the
+device buffers, checks dtype/device/contiguity/size on the host, passes raw
+pointers and the current HIP stream to the C entry point of the same name,
+and raises MoEError on a non-zero status.  All arithmetic of the forward runs
+in the library's HIP kernels.  There is no fallback: if the library is not
+built, importing this module raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_native.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_native.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it first (python -m mixture_experts_expert_amd.build "
+        "or __graft_entry__.build()); there is no non-HIP fallback")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _f64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+
+_SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moe_source_capacity": (_i64, [_i64, _i32, _i32, _f64]),
+    "moe_layout_block_m": (_i32, []),
+    "moe_padded_capacity": (_i64, [_i64]),
+    "moe_route_capacity": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "moe_align": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i64,
+                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_grouped_ffn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64,
+                                           _vp, _vp, _vp]),
+    "moe_grouped_fc1_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64,
+                                              _vp, _vp]),
+    "moe_grouped_fc2": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _vp]),
+    "moe_gather_combine": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i64, _vp, _vp]),
+}
+for _name, (_res, _args) in _SIGNATURES.items():
+    _fn = getattr(lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+def header_functions(path: str = HEADER_PATH):
+    """Names of the functions include/moe_native.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {moe_status_string(status)} ({status})")
+        self.status = status
+
+
+def moe_status_string(status: int) -> str:
+    return lib.moe_status_string(int(status)).decode()
+
+
+def moe_source_capacity(N: int, K: int, E: int, F: float) -> int:
+    c = lib.moe_source_capacity(int(N), int(K), int(E), float(F))
+    if c < 0:
+        raise MoEError("moe_source_capacity", c)
+    return int(c)
+
+
+def moe_layout_block_m() -> int:
+    return int(lib.moe_layout_block_m())
+
+
+def moe_padded_capacity(C: int) -> int:
+    c = lib.moe_padded_capacity(int(C))
+    if c < 0:
+        raise MoEError("moe_padded_capacity", c)
+    return int(c)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _ptr(t: torch.Tensor, dtype: torch.dtype, numel: int, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoEError(fn, status)
+
+
+def moe_route_capacity(logits, K: int, C: int, topk_ids, topk_probs, route_slot, expert_count,
+                       stream=None):
+    N, E = logits.shape
+    _check("moe_route_capacity", lib.moe_route_capacity(
+        _ptr(logits, torch.float32, N * E, "logits"), N, E, K, C,
+        _ptr(topk_ids, torch.int32, N * K, "topk_ids"),
+        _ptr(topk_probs, torch.float32, N * K, "topk_probs"),
+        _ptr(route_slot, torch.int32, N * K, "route_slot"),
+        _ptr(expert_count, torch.int32, E, "expert_count"), _stream(stream)))
+
+
+def moe_align(topk_ids, topk_probs, route_slot, expert_count, N: int, E: int, K: int, C: int,
+              sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
+              token_route_count, num_tokens_post_padded, stream=None):
+    R = E * moe_padded_capacity(C)
+    BM = moe_layout_block_m()
+    _check("moe_align", lib.moe_align(
+        _ptr(topk_ids, torch.int32, N * K, "topk_ids"),
+        _ptr(topk_probs, torch.float32, N * K, "topk_probs"),
+        _ptr(route_slot, torch.int32, N * K, "route_slot"),
+        _ptr(expert_count, torch.int32, E, "expert_count"), N, E, K, C,
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"),
+        _ptr(slot_probs, torch.float32, R, "slot_probs"),
+        _ptr(expert_ids, torch.int32, R // BM, "expert_ids"),
+        _ptr(block_start, torch.int32, E, "block_start"),
+        _ptr(token_routes, torch.int32, N * K, "token_routes"),
+        _ptr(token_route_count, torch.int32, N, "token_route_count"),
+        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"), _stream(stream)))
+
+
+def moe_grouped_ffn_fwd(x, w1, w2, sorted_slot_ids, slot_probs, C: int, act, route_out,
+                        stream=None):
+    N, H = x.shape
+    E, I2, H1 = w1.shape
+    I = I2 // 2
+    if H1 != H or tuple(w2.shape) != (E, H, I) or I2 != 2 * I:
+        raise ValueError("weights must be w1 [E, 2I, H] and w2 [E, H, I]")
+    R = E * moe_padded_capacity(C)
+    _check("moe_grouped_ffn_fwd", lib.moe_grouped_ffn_fwd(
+        _ptr(x, torch.bfloat16, N * H, "x"), _ptr(w1, torch.bfloat16, E * 2 * I * H, "w1"),
+        _ptr(w2, torch.bfloat16, E * H * I, "w2"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"),
+        _ptr(slot_probs, torch.float32, R, "slot_probs"), N, H, I, E, C,
+        _ptr(act, torch.bfloat16, R * I, "act"), _ptr(route_out, torch.bfloat16, R * H, "route_out"),
+        _stream(stream)))
+
+
+def moe_grouped_fc1_swiglu(x, w1, sorted_slot_ids, slot_probs, C: int, act, stream=None):
+    N, H = x.shape
+    E, I2, H1 = w1.shape
+    I = I2 // 2
+    if H1 != H or I2 != 2 * I:
+        raise ValueError("w1 must be [E, 2I, H]")
+    R = E * moe_padded_capacity(C)
+    _check("moe_grouped_fc1_swiglu", lib.moe_grouped_fc1_swiglu(
+        _ptr(x, torch.bfloat16, N * H, "x"), _ptr(w1, torch.bfloat16, E * 2 * I * H, "w1"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"),
+        _ptr(slot_probs, torch.float32, R, "slot_probs"), N, H, I, E, C,
+        _ptr(act, torch.bfloat16, R * I, "act"), _stream(stream)))
+
+
+def moe_grouped_fc2(act, w2, N: int, C: int, route_out, stream=None):
+    E, H, I = w2.shape
+    R = E * moe_padded_capacity(C)
+    _check("moe_grouped_fc2", lib.moe_grouped_fc2(
+        _ptr(act, torch.bfloat16, R * I, "act"), _ptr(w2, torch.bfloat16, E * H * I, "w2"),
+        N, H, I, E, C, _ptr(route_out, torch.bfloat16, R * H, "route_out"), _stream(stream)))
+
+
+def moe_gather_combine(route_out, token_routes, y, stream=None):
+    N, K = token_routes.shape
+    R, H = route_out.shape
+    _check("moe_gather_combine", lib.moe_gather_combine(
+        _ptr(route_out, torch.bfloat16, R * H, "route_out"),
+        _ptr(token_routes, torch.int32, N * K, "token_routes"), N, K, H, R,
+        _ptr(y, torch.bfloat16, N * H, "y"), _stream(stream)))

@@ -1,0 +1,81 @@
+// Internal helpers shared by the HIP sources of libmoe_native (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe_native.h"
+
+namespace moe {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kBlockM = 32;        // route-list layout block (BM)
+constexpr int64_t kMaxN = 16384;   // tokens per call (capacity selection holds an expert's candidates in LDS)
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 32;
+constexpr int kMaxDim = 16384;     // H and I
+
+// ---------------------------------------------------------------- host-side checks
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline int launch_status() {
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+// Shape checks shared by the entry points; C must equal moe_source_capacity's value.
+int check_route_shape(int64_t N, int32_t E, int32_t K, int64_t C);
+int check_dims(int32_t H, int32_t I);
+
+// ---------------------------------------------------------------- device helpers
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float32 -> bf16 (finite inputs; NaN is out of contract).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Inclusive prefix sum across the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        int o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over a whole block (blockDim.x a multiple of 64, at
+// most 1024 threads).  `scratch` must hold 16 ints in LDS; returns this
+// thread's exclusive prefix and writes the block total to *total.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+    const int lane = lane_id();
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    int inc = wave_inclusive_scan(v);
+    if (lane == kWave - 1) scratch[wave] = inc;
+    __syncthreads();
+    int base = 0, tot = 0;
+    for (int w = 0; w < nwaves; ++w) {
+        int c = scratch[w];
+        if (w < wave) base += c;
+        tot += c;
+    }
+    __syncthreads();   // scratch may be reused right after
+    *total = tot;
+    return base + inc - v;
+}
+
+}  // namespace moe

@@ -10,6 +10,15 @@ if ROOT not in sys.path:
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
+# The suite loads the in-tree library; it builds it only when nothing is built.
+if not os.path.exists(os.path.join(ROOT, "mixture_experts_expert_amd", "libmoe_native.so")):
+    import importlib.util as _ilu   # the package itself refuses to import unbuilt
+    _spec = _ilu.spec_from_file_location(
+        "_moe_build", os.path.join(ROOT, "mixture_experts_expert_amd", "build.py"))
+    _build = _ilu.module_from_spec(_spec)
+    _spec.loader.exec_module(_build)
+    _build.build(verbose=True)
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")

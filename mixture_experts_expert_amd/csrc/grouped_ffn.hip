@@ -37,7 +37,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBK = 64;          // K slab (bf16 elements) per LDS stage: 128 bytes per row
+constexpr int kBK = 32;          // K slab (bf16 elements) per LDS stage: 64 bytes per tile row
 constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (CDNA)
 
@@ -61,13 +61,45 @@ __device__ __forceinline__ int xcd_remap(int bid, int G) {
     return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
 }
 
-// byte offset of 16-byte chunk c of LDS row r (128-byte rows)
-__device__ __forceinline__ uint32_t lds_off(int r, int c) {
-    return static_cast<uint32_t>(r * 128 + ((c ^ (r & 7)) << 4));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: base, stride 0, num_records = bytes, 32-bit data format.
+// A load whose offset (everything is passed in the per-lane voffset, which the
+// range check covers) lies at or beyond `bytes` returns zeros and touches no
+// memory: this is how the sentinel row N and rows past an expert's segment
+// read as zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    r.x = static_cast<int>(static_cast<uint32_t>(a));
+    r.y = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu);
+    r.z = static_cast<int>(bytes);
+    r.w = kRsrcWord3;
+    return r;
 }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRsrcWord3);
+// LDS byte address of a __shared__ object (what M0 and ds_* instructions use).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) void*)p));
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane L's data lands
+// at M0 + 16*L, so one wave fills one contiguous kilobyte.  Issued as inline
+// assembly so the compiler neither tracks it (it would otherwise wait for every
+// pending LDS-bound load before any LDS read) nor reorders it across the
+// explicit waits below ("memory" clobber).
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                 : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
 }
 
 __device__ __forceinline__ float silu(float g) {
@@ -76,23 +108,44 @@ __device__ __forceinline__ float silu(float g) {
     return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-template <int BMT, int BNT, int WM, int WN, bool FC1>
+// LDS layout of one stage: tile row r (64 bytes = four 16-byte K chunks) at
+// r*64; logical chunk c sits at physical chunk c ^ ((r >> 2) & 3).  An MFMA
+// operand read has 16 consecutive lanes fetch one chunk of 16 consecutive
+// rows; with 64 four-byte banks the swizzle spreads them over all 256 bytes.
+__device__ __forceinline__ uint32_t lds_off(int r, int c) {
+    return static_cast<uint32_t>(r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
+}
+
+template <int BMT, int BNT, int WM, int WN, int NA, int NB, bool FC1>
 __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
-    constexpr int NTHR = WM * WN * kWave;
+    constexpr int NW = WM * WN;
+    constexpr int NTHR = NW * kWave;
     constexpr int WTM = BMT / WM;
     constexpr int WTN = BNT / WN;
     constexpr int MI = WTM / 32;
     constexpr int NI = WTN / 32;
-    constexpr int NIH = NI / 2;
-    constexpr int A_PER = BMT * 8 / NTHR;
-    constexpr int B_PER = BNT * 8 / NTHR;
-    static_assert(MI >= 1 && NI >= 1 && A_PER >= 1 && B_PER >= 1, "tile too small");
-    static_assert(!FC1 || NI % 2 == 0, "FC1 waves need matching gate and up blocks");
-    static_assert(BMT * 8 % NTHR == 0 && BNT * 8 % NTHR == 0, "uneven tile load");
+    constexpr int ROWB = kBK * 2;                          // bytes of a tile row per stage
+    constexpr int A_STAGE = BMT * ROWB;
+    constexpr int B_STAGE = BNT * ROWB;
+    constexpr int B_RING = NA * A_STAGE;                   // the B ring follows the A ring
+    constexpr int A_INST = BMT / 16 / NW;                  // 1 KB (16 rows) DMA loads per wave
+    constexpr int B_INST = BNT / 16 / NW;
+    constexpr int LOADS = A_INST + B_INST;                 // per wave per K slab
+    constexpr int OUT_COLS = FC1 ? BNT / 2 : BNT;          // output columns of this tile
+    constexpr int OUT_PITCH = OUT_COLS * 2 + 16;           // padded bf16 row of the staged output
+    constexpr int RINGS = NA * A_STAGE + NB * B_STAGE;
+    constexpr int LDS_BYTES = RINGS > BMT * OUT_PITCH ? RINGS : BMT * OUT_PITCH;
+    // At step kt the newest load that must have landed is A(kt) (B(kt) was
+    // issued NB-NA steps earlier).  Issued after it: B(kt+NB-NA) in the same
+    // step, then NA-2 whole steps; loads complete in issue order.
+    constexpr int WAIT = B_INST + (NA - 2) * LOADS;
+    static_assert(MI >= 1 && NI >= 1, "tile too small");
+    static_assert(A_INST >= 1 && B_INST >= 1 && BMT % (16 * NW) == 0 && BNT % (16 * NW) == 0,
+                  "whole 16-row DMA blocks per wave");
+    static_assert(NA >= 2 && NB >= NA && WAIT < 64, "stage rings");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
-    __shared__ __attribute__((aligned(16))) uint8_t sA[BMT * kBK * 2];
-    __shared__ __attribute__((aligned(16))) uint8_t sB[BNT * kBK * 2];
-    __shared__ float s_prob[FC1 ? BMT : 1];
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -107,21 +160,26 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     const int m0 = mt * BMT;
     const int64_t slot0 = static_cast<int64_t>(e) * p.Cp + m0;   // first slot of this tile
 
-    // ---- operand descriptors and per-thread row offsets (fixed over the K loop)
-    __amdgpu_buffer_rsrc_t ra_rsrc, rb_rsrc;
+    // ---- DMA addressing.  Wave w's load i covers the 16 tile rows of block
+    // q = w + i*NW; lane L brings row 16q + L/4, physical chunk L&3, i.e.
+    // logical chunk (L&3) ^ (L>>4) (the swizzle of row 16q + L/4).
+    const int lrow = lane >> 2;
+    const uint32_t lchunk = static_cast<uint32_t>((lane & 3) ^ (lane >> 4));
+    const uint32_t row_bytes = static_cast<uint32_t>(p.Kdim) * 2u;
+    i32x4 ra_rsrc, rb_rsrc;
     if (FC1) {
-        ra_rsrc = make_rsrc(p.a, static_cast<uint32_t>(p.N) * p.Kdim * 2u);
+        ra_rsrc = make_rsrc(p.a, static_cast<uint32_t>(p.N) * row_bytes);
     } else {
         ra_rsrc = make_rsrc(p.a + static_cast<int64_t>(e) * p.Cp * p.Kdim,
-                            static_cast<uint32_t>(p.Cp) * p.Kdim * 2u);
+                            static_cast<uint32_t>(p.Cp) * row_bytes);
     }
     rb_rsrc = make_rsrc(p.w + static_cast<int64_t>(e) * p.wrows * p.Kdim,
-                        static_cast<uint32_t>(p.wrows) * p.Kdim * 2u);
+                        static_cast<uint32_t>(p.wrows) * row_bytes);
 
-    uint32_t a_goff[A_PER], a_loff[A_PER], b_goff[B_PER], b_loff[B_PER];
+    uint32_t a_voff[A_INST], b_voff[B_INST];
 #pragma unroll
-    for (int i = 0; i < A_PER; ++i) {
-        const int q = tid + i * NTHR, r = q >> 3, c = q & 7;
+    for (int i = 0; i < A_INST; ++i) {
+        const int r = 16 * (wave + i * NW) + lrow;
         int row;
         if (FC1) {
             row = p.N;   // sentinel: outside the descriptor, reads zeros
@@ -132,26 +190,35 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         } else {
             row = m0 + r;   // rows past Cp lie outside the expert's descriptor
         }
-        a_goff[i] = static_cast<uint32_t>(row) * p.Kdim * 2u + c * 16u;
-        a_loff[i] = lds_off(r, c);
+        a_voff[i] = static_cast<uint32_t>(row) * row_bytes + lchunk * 16u;
     }
 #pragma unroll
-    for (int i = 0; i < B_PER; ++i) {
-        const int q = tid + i * NTHR, r = q >> 3, c = q & 7;
+    for (int i = 0; i < B_INST; ++i) {
+        const int q = wave + i * NW;
         int wrow;
         if (FC1) {
-            const int j0 = nt * (BNT / 2);
-            wrow = r < BNT / 2 ? j0 + r : p.ncols + j0 + (r - BNT / 2);
+            // FC1's B tile interleaves 16 gate rows and the 16 matching up rows
+            // in each 32-row MFMA block, so one accumulator block carries both.
+            wrow = ((q & 1) ? p.ncols : 0) + nt * (BNT / 2) + (q >> 1) * 16 + lrow;
         } else {
-            wrow = nt * BNT + r;
+            wrow = nt * BNT + 16 * q + lrow;
         }
-        b_goff[i] = static_cast<uint32_t>(wrow) * p.Kdim * 2u + c * 16u;
-        b_loff[i] = lds_off(r, c);
+        b_voff[i] = static_cast<uint32_t>(wrow) * row_bytes + lchunk * 16u;
     }
-    if (FC1) {
-        for (int i = tid; i < BMT; i += NTHR)
-            s_prob[i] = m0 + i < p.Cp ? p.slot_probs[slot0 + i] : 0.0f;
-    }
+    const uint32_t lds0 = lds_addr(smem);
+
+    auto issue_a = [&](int buf, int kt) {
+        const uint32_t koff = static_cast<uint32_t>(kt) * ROWB;
+        const uint32_t st = lds0 + buf * A_STAGE;
+#pragma unroll
+        for (int i = 0; i < A_INST; ++i) dma16(ra_rsrc, a_voff[i] + koff, st + (wave + i * NW) * 1024);
+    };
+    auto issue_b = [&](int buf, int kt) {
+        const uint32_t koff = static_cast<uint32_t>(kt) * ROWB;
+        const uint32_t st = lds0 + B_RING + buf * B_STAGE;
+#pragma unroll
+        for (int i = 0; i < B_INST; ++i) dma16(rb_rsrc, b_voff[i] + koff, st + (wave + i * NW) * 1024);
+    };
 
     floatx16 acc[MI][NI];
 #pragma unroll
@@ -161,102 +228,123 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
 #pragma unroll
             for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
 
-    u32x4 ra[A_PER], rb[B_PER];
-    auto gload = [&](int kt) {
-        const uint32_t koff = static_cast<uint32_t>(kt) * kBK * 2u;
-#pragma unroll
-        for (int i = 0; i < A_PER; ++i)
-            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(ra_rsrc, a_goff[i] + koff, 0, 0);
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i)
-            rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rb_rsrc, b_goff[i] + koff, 0, 0);
-    };
-
-    // B-tile LDS row of block ni for this wave (FC1: gate blocks, then up blocks)
-    auto b_row = [&](int ni) {
-        if (FC1) {
-            return ni < NIH ? wn * (WTN / 2) + ni * 32 : BNT / 2 + wn * (WTN / 2) + (ni - NIH) * 32;
-        }
-        return wn * WTN + ni * 32;
-    };
-
-    const int KT = p.Kdim / kBK;
-    gload(0);
-    for (int kt = 0; kt < KT; ++kt) {
-        __syncthreads();
-#pragma unroll
-        for (int i = 0; i < A_PER; ++i) *reinterpret_cast<u32x4*>(sA + a_loff[i]) = ra[i];
-#pragma unroll
-        for (int i = 0; i < B_PER; ++i) *reinterpret_cast<u32x4*>(sB + b_loff[i]) = rb[i];
-        __syncthreads();
-        if (kt + 1 < KT) gload(kt + 1);
+    auto compute = [&](int abuf, int bbuf) {
+        const uint8_t* sA = smem + abuf * A_STAGE;
+        const uint8_t* sB = smem + B_RING + bbuf * B_STAGE;
 #pragma unroll
         for (int ks = 0; ks < kBK / 16; ++ks) {
             const int c = ks * 2 + (lane >> 5);
             bf16x8 af[MI], bfr[NI];
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi) {
-                const int r = wm * WTM + mi * 32 + (lane & 31);
-                af[mi] = *reinterpret_cast<const bf16x8*>(sA + lds_off(r, c));
-            }
+            for (int mi = 0; mi < MI; ++mi)
+                af[mi] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * WTM + mi * 32 + (lane & 31), c));
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                const int r = b_row(ni) + (lane & 31);
-                bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + lds_off(r, c));
-            }
+            for (int ni = 0; ni < NI; ++ni)
+                bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + lds_off(wn * WTN + ni * 32 + (lane & 31), c));
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
         }
+    };
+
+    // ---- K loop over two LDS rings: the gathered A slabs (L2/MALL hits, short
+    // latency) NA deep, the weight slabs (the HBM stream) NB deep, so NB-1
+    // weight slabs are in flight while one is consumed.  Step j issues
+    // A(j+NA-1) then B(j+NB-1); the prologue replays steps -(NB-1)..-1.
+    // Loads past the end of K are issued anyway (they read the next row or,
+    // past the descriptor, zeros, into stages never computed) so every step
+    // waits for the same count.  The barrier after the wait publishes slab kt
+    // and retires slab kt-1, whose stages the new loads overwrite.
+    const int KT = p.Kdim / kBK;
+    __syncthreads();   // the token rows are read; the rings are free
+#pragma unroll
+    for (int j = -(NB - 1); j < 0; ++j) {
+        if (j + NA - 1 >= 0) issue_a(j + NA - 1, j + NA - 1);
+        issue_b(j + NB - 1, j + NB - 1);
     }
+    int abuf = 0, bbuf = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+        wait_vmcnt<WAIT>();
+        __syncthreads();
+        issue_a(abuf == 0 ? NA - 1 : abuf - 1, kt + NA - 1);   // stage (kt + NA - 1) % NA
+        issue_b(bbuf == 0 ? NB - 1 : bbuf - 1, kt + NB - 1);
+        compute(abuf, bbuf);
+        abuf = abuf + 1 == NA ? 0 : abuf + 1;
+        bbuf = bbuf + 1 == NB ? 0 : bbuf + 1;
+    }
+    wait_vmcnt<0>();   // no DMA may land in the LDS the epilogue reuses
+    __syncthreads();
 
     // ---- epilogue.  32x32 accumulator layout: lane holds column (lane & 31)
-    // and rows 8*(j/4) + 4*(lane/32) + (j%4), j = 0..15.
+    // and rows 8*(j/4) + 4*(lane/32) + (j%4), j = 0..15.  The bf16 tile is
+    // staged in LDS (rows padded by 16 bytes) and written out in 16-byte
+    // chunks along rows.
     const int row_lane = 4 * (lane >> 5);
     const int col_lane = lane & 31;
     if (FC1) {
-        const int I = p.ncols;
-        const int j0 = nt * (BNT / 2);
+        // Lane l (column l&31 of a block) holds gate if (l & 16) == 0, else the
+        // up value of column l^16.  Partners swap every value and both form the
+        // activation.  (Selecting values, never vector elements, keeps the
+        // compiler from building a dynamic element index.)
+        const bool gate_lane = (lane & 16) == 0;
+        float prob[MI][16];   // routing probability of each accumulator row (0 past Cp)
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-            for (int nh = 0; nh < NIH; ++nh) {
-                const int col = j0 + wn * (WTN / 2) + nh * 32 + col_lane;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int row = wm * WTM + mi * 32 + 8 * (j >> 2) + row_lane + (j & 3);
-                    if (m0 + row < p.Cp && col < I) {
-                        const float g = acc[mi][nh][j], u = acc[mi][nh + NIH][j];
-                        p.out[(slot0 + row) * I + col] = f32_to_bf16(silu(g) * u * s_prob[row]);
-                    }
-                }
+            for (int j = 0; j < 16; ++j) {
+                const int row = wm * WTM + mi * 32 + 8 * (j >> 2) + row_lane + (j & 3);
+                prob[mi][j] = m0 + row < p.Cp ? p.slot_probs[slot0 + row] : 0.0f;
             }
-    } else {
-        const int H = p.ncols;
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) {
-                const int col = nt * BNT + wn * WTN + ni * 32 + col_lane;
+                const int col = (wn * WTN + ni * 32) / 2 + (lane & 15);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const float mine = acc[mi][ni][j];
+                    const float other = __shfl_xor(mine, 16, kWave);
+                    const float g = gate_lane ? mine : other;
+                    const float u = gate_lane ? other : mine;
+                    const int row = wm * WTM + mi * 32 + 8 * (j >> 2) + row_lane + (j & 3);
+                    // both partners form the same value and store it to the same place
+                    *reinterpret_cast<uint16_t*>(smem + row * OUT_PITCH + col * 2) =
+                        f32_to_bf16(silu(g) * u * prob[mi][j]);
+                }
+            }
+    } else {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const int col = wn * WTN + ni * 32 + col_lane;
 #pragma unroll
                 for (int j = 0; j < 16; ++j) {
                     const int row = wm * WTM + mi * 32 + 8 * (j >> 2) + row_lane + (j & 3);
-                    if (m0 + row < p.Cp && col < H)
-                        p.out[(slot0 + row) * H + col] = f32_to_bf16(acc[mi][ni][j]);
+                    *reinterpret_cast<uint16_t*>(smem + row * OUT_PITCH + col * 2) = f32_to_bf16(acc[mi][ni][j]);
                 }
             }
     }
+    __syncthreads();
+    constexpr int CPR = OUT_COLS / 8;            // 16-byte chunks per output row
+    const int col0 = nt * OUT_COLS;
+    for (int q = tid; q < BMT * CPR; q += NTHR) {
+        const int r = q / CPR, c = q - r * CPR;
+        if (m0 + r < p.Cp && col0 + c * 8 < p.ncols)
+            *reinterpret_cast<u32x4*>(p.out + (slot0 + r) * p.ncols + col0 + c * 8) =
+                *reinterpret_cast<const u32x4*>(smem + r * OUT_PITCH + c * 16);
+    }
 }
 
-template <int BMT, int BNT, int WM, int WN>
+template <int BMT, int BNT, int WM, int WN, int NA, int NB>
 void launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s) {
     a.MT = (a.Cp + BMT - 1) / BMT;
     a.NT = fc1 ? (a.ncols + BNT / 2 - 1) / (BNT / 2) : (a.ncols + BNT - 1) / BNT;
     const int grid = E * a.MT * a.NT;
-    if (fc1) ffn_gemm_kernel<BMT, BNT, WM, WN, true><<<grid, WM * WN * kWave, 0, s>>>(a);
-    else ffn_gemm_kernel<BMT, BNT, WM, WN, false><<<grid, WM * WN * kWave, 0, s>>>(a);
+    if (fc1) ffn_gemm_kernel<BMT, BNT, WM, WN, NA, NB, true><<<grid, WM * WN * kWave, 0, s>>>(a);
+    else ffn_gemm_kernel<BMT, BNT, WM, WN, NA, NB, false><<<grid, WM * WN * kWave, 0, s>>>(a);
 }
 
 // M-tile: the one (of 256, 128, 64, 32) that pads Cp the least; ties go to
@@ -272,10 +360,10 @@ int pick_tile_m(int Cp) {
 
 void launch(const FfnArgs& a, bool fc1, int E, hipStream_t s) {
     switch (pick_tile_m(a.Cp)) {
-        case 256: launch_gemm<256, 256, 2, 4>(a, fc1, E, s); break;
-        case 128: launch_gemm<128, 256, 2, 4>(a, fc1, E, s); break;
-        case 64: launch_gemm<64, 128, 2, 2>(a, fc1, E, s); break;
-        default: launch_gemm<32, 128, 1, 2>(a, fc1, E, s); break;
+        case 256: launch_gemm<256, 256, 2, 4, 3, 7>(a, fc1, E, s); break;
+        case 128: launch_gemm<128, 256, 2, 4, 3, 7>(a, fc1, E, s); break;
+        case 64: launch_gemm<64, 128, 2, 2, 3, 7>(a, fc1, E, s); break;
+        default: launch_gemm<32, 128, 1, 2, 3, 7>(a, fc1, E, s); break;
     }
 }
 

@@ -37,7 +37,6 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kBK = 32;          // K slab (bf16 elements) per LDS stage: 64 bytes per tile row
 constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (CDNA)
 
@@ -71,9 +70,10 @@ typedef int i32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
     i32x4 r;
-    r.x = static_cast<int>(static_cast<uint32_t>(a));
-    r.y = static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu);
-    r.z = static_cast<int>(bytes);
+    // the descriptor lives in scalar registers: every lane holds the same value
+    r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+    r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu));
+    r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
     r.w = kRsrcWord3;
     return r;
 }
@@ -108,15 +108,18 @@ __device__ __forceinline__ float silu(float g) {
     return g * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
-// LDS layout of one stage: tile row r (64 bytes = four 16-byte K chunks) at
-// r*64; logical chunk c sits at physical chunk c ^ ((r >> 2) & 3).  An MFMA
-// operand read has 16 consecutive lanes fetch one chunk of 16 consecutive
-// rows; with 64 four-byte banks the swizzle spreads them over all 256 bytes.
+// LDS layout of one stage: tile row r (ROWB = 2*BK bytes, CPR = ROWB/16
+// chunks of 8 K values) at r*ROWB; logical chunk c sits at physical chunk
+// c ^ ((r / RP) % CPR) with RP = 256/ROWB rows per 256 bytes.  An MFMA operand
+// read has 16 consecutive lanes fetch one chunk of 16 consecutive rows; with
+// 64 four-byte banks the swizzle spreads them over all 256 bytes.
+template <int BK>
 __device__ __forceinline__ uint32_t lds_off(int r, int c) {
-    return static_cast<uint32_t>(r * 64 + ((c ^ ((r >> 2) & 3)) << 4));
+    constexpr int ROWB = BK * 2, CPR = ROWB / 16, RP = 256 / ROWB;
+    return static_cast<uint32_t>(r * ROWB + ((c ^ ((r / RP) % CPR)) << 4));
 }
 
-template <int BMT, int BNT, int WM, int WN, int NA, int NB, bool FC1>
+template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1>
 __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     constexpr int NW = WM * WN;
     constexpr int NTHR = NW * kWave;
@@ -124,12 +127,14 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     constexpr int WTN = BNT / WN;
     constexpr int MI = WTM / 32;
     constexpr int NI = WTN / 32;
-    constexpr int ROWB = kBK * 2;                          // bytes of a tile row per stage
+    constexpr int ROWB = BK * 2;                           // bytes of a tile row per stage
+    constexpr int CPR = ROWB / 16;                         // 16-byte chunks per tile row
+    constexpr int RPI = 1024 / ROWB;                       // tile rows per 1 KB DMA load
     constexpr int A_STAGE = BMT * ROWB;
     constexpr int B_STAGE = BNT * ROWB;
     constexpr int B_RING = NA * A_STAGE;                   // the B ring follows the A ring
-    constexpr int A_INST = BMT / 16 / NW;                  // 1 KB (16 rows) DMA loads per wave
-    constexpr int B_INST = BNT / 16 / NW;
+    constexpr int A_INST = BMT / RPI / NW;                 // DMA loads per wave per stage
+    constexpr int B_INST = BNT / RPI / NW;
     constexpr int LOADS = A_INST + B_INST;                 // per wave per K slab
     constexpr int OUT_COLS = FC1 ? BNT / 2 : BNT;          // output columns of this tile
     constexpr int OUT_PITCH = OUT_COLS * 2 + 16;           // padded bf16 row of the staged output
@@ -140,8 +145,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     // step, then NA-2 whole steps; loads complete in issue order.
     constexpr int WAIT = B_INST + (NA - 2) * LOADS;
     static_assert(MI >= 1 && NI >= 1, "tile too small");
-    static_assert(A_INST >= 1 && B_INST >= 1 && BMT % (16 * NW) == 0 && BNT % (16 * NW) == 0,
-                  "whole 16-row DMA blocks per wave");
+    static_assert(BK == 32 || BK == 64, "K slab");
+    static_assert(A_INST >= 1 && B_INST >= 1 && BMT % (RPI * NW) == 0 && BNT % (RPI * NW) == 0,
+                  "whole DMA blocks per wave");
     static_assert(NA >= 2 && NB >= NA && WAIT < 64, "stage rings");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
@@ -160,11 +166,14 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     const int m0 = mt * BMT;
     const int64_t slot0 = static_cast<int64_t>(e) * p.Cp + m0;   // first slot of this tile
 
-    // ---- DMA addressing.  Wave w's load i covers the 16 tile rows of block
-    // q = w + i*NW; lane L brings row 16q + L/4, physical chunk L&3, i.e.
-    // logical chunk (L&3) ^ (L>>4) (the swizzle of row 16q + L/4).
-    const int lrow = lane >> 2;
-    const uint32_t lchunk = static_cast<uint32_t>((lane & 3) ^ (lane >> 4));
+    // ---- DMA addressing.  Wave w's load i covers the RPI tile rows of block
+    // q = w + i*NW; lane L brings row RPI*q + L/CPR, physical chunk L%CPR,
+    // i.e. the logical chunk that the swizzle of that row puts there.
+    const int lrow = lane / CPR;
+    auto lchunk = [&](int q) -> uint32_t {
+        const int r = RPI * q + lrow;
+        return static_cast<uint32_t>((lane % CPR) ^ ((r / (256 / ROWB)) % CPR));
+    };
     const uint32_t row_bytes = static_cast<uint32_t>(p.Kdim) * 2u;
     i32x4 ra_rsrc, rb_rsrc;
     if (FC1) {
@@ -179,7 +188,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     uint32_t a_voff[A_INST], b_voff[B_INST];
 #pragma unroll
     for (int i = 0; i < A_INST; ++i) {
-        const int r = 16 * (wave + i * NW) + lrow;
+        const int q = wave + i * NW;
+        const int r = RPI * q + lrow;
         int row;
         if (FC1) {
             row = p.N;   // sentinel: outside the descriptor, reads zeros
@@ -190,20 +200,22 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         } else {
             row = m0 + r;   // rows past Cp lie outside the expert's descriptor
         }
-        a_voff[i] = static_cast<uint32_t>(row) * row_bytes + lchunk * 16u;
+        a_voff[i] = static_cast<uint32_t>(row) * row_bytes + lchunk(q) * 16u;
     }
 #pragma unroll
     for (int i = 0; i < B_INST; ++i) {
         const int q = wave + i * NW;
+        const int R = RPI * q + lrow;                    // tile row
         int wrow;
         if (FC1) {
             // FC1's B tile interleaves 16 gate rows and the 16 matching up rows
             // in each 32-row MFMA block, so one accumulator block carries both.
-            wrow = ((q & 1) ? p.ncols : 0) + nt * (BNT / 2) + (q >> 1) * 16 + lrow;
+            const int w = R & 31;
+            wrow = (w < 16 ? 0 : p.ncols) + nt * (BNT / 2) + (R >> 5) * 16 + (w & 15);
         } else {
-            wrow = nt * BNT + 16 * q + lrow;
+            wrow = nt * BNT + R;
         }
-        b_voff[i] = static_cast<uint32_t>(wrow) * row_bytes + lchunk * 16u;
+        b_voff[i] = static_cast<uint32_t>(wrow) * row_bytes + lchunk(q) * 16u;
     }
     const uint32_t lds0 = lds_addr(smem);
 
@@ -232,15 +244,15 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         const uint8_t* sA = smem + abuf * A_STAGE;
         const uint8_t* sB = smem + B_RING + bbuf * B_STAGE;
 #pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
+        for (int ks = 0; ks < BK / 16; ++ks) {
             const int c = ks * 2 + (lane >> 5);
             bf16x8 af[MI], bfr[NI];
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
-                af[mi] = *reinterpret_cast<const bf16x8*>(sA + lds_off(wm * WTM + mi * 32 + (lane & 31), c));
+                af[mi] = *reinterpret_cast<const bf16x8*>(sA + lds_off<BK>(wm * WTM + mi * 32 + (lane & 31), c));
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni)
-                bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + lds_off(wn * WTN + ni * 32 + (lane & 31), c));
+                bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + lds_off<BK>(wn * WTN + ni * 32 + (lane & 31), c));
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
@@ -257,7 +269,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     // past the descriptor, zeros, into stages never computed) so every step
     // waits for the same count.  The barrier after the wait publishes slab kt
     // and retires slab kt-1, whose stages the new loads overwrite.
-    const int KT = p.Kdim / kBK;
+    const int KT = p.Kdim / BK;
     __syncthreads();   // the token rows are read; the rings are free
 #pragma unroll
     for (int j = -(NB - 1); j < 0; ++j) {
@@ -328,23 +340,23 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
             }
     }
     __syncthreads();
-    constexpr int CPR = OUT_COLS / 8;            // 16-byte chunks per output row
+    constexpr int OCPR = OUT_COLS / 8;           // 16-byte chunks per output row
     const int col0 = nt * OUT_COLS;
-    for (int q = tid; q < BMT * CPR; q += NTHR) {
-        const int r = q / CPR, c = q - r * CPR;
+    for (int q = tid; q < BMT * OCPR; q += NTHR) {
+        const int r = q / OCPR, c = q - r * OCPR;
         if (m0 + r < p.Cp && col0 + c * 8 < p.ncols)
             *reinterpret_cast<u32x4*>(p.out + (slot0 + r) * p.ncols + col0 + c * 8) =
                 *reinterpret_cast<const u32x4*>(smem + r * OUT_PITCH + c * 16);
     }
 }
 
-template <int BMT, int BNT, int WM, int WN, int NA, int NB>
+template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB>
 void launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s) {
     a.MT = (a.Cp + BMT - 1) / BMT;
     a.NT = fc1 ? (a.ncols + BNT / 2 - 1) / (BNT / 2) : (a.ncols + BNT - 1) / BNT;
     const int grid = E * a.MT * a.NT;
-    if (fc1) ffn_gemm_kernel<BMT, BNT, WM, WN, NA, NB, true><<<grid, WM * WN * kWave, 0, s>>>(a);
-    else ffn_gemm_kernel<BMT, BNT, WM, WN, NA, NB, false><<<grid, WM * WN * kWave, 0, s>>>(a);
+    if (fc1) ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, true><<<grid, WM * WN * kWave, 0, s>>>(a);
+    else ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, false><<<grid, WM * WN * kWave, 0, s>>>(a);
 }
 
 // M-tile: the one (of 256, 128, 64, 32) that pads Cp the least; ties go to
@@ -360,10 +372,12 @@ int pick_tile_m(int Cp) {
 
 void launch(const FfnArgs& a, bool fc1, int E, hipStream_t s) {
     switch (pick_tile_m(a.Cp)) {
-        case 256: launch_gemm<256, 256, 2, 4, 3, 7>(a, fc1, E, s); break;
-        case 128: launch_gemm<128, 256, 2, 4, 3, 7>(a, fc1, E, s); break;
-        case 64: launch_gemm<64, 128, 2, 2, 3, 7>(a, fc1, E, s); break;
-        default: launch_gemm<32, 128, 1, 2, 3, 7>(a, fc1, E, s); break;
+        // 64-wide K slabs (128 contiguous bytes per weight row per step keep the
+        // HBM stream efficient); rings sized to the 160 KB LDS.
+        case 256: launch_gemm<256, 256, 2, 4, 64, 2, 3>(a, fc1, E, s); break;
+        case 128: launch_gemm<128, 256, 2, 4, 64, 2, 3>(a, fc1, E, s); break;
+        case 64: launch_gemm<64, 128, 2, 2, 64, 2, 3>(a, fc1, E, s); break;
+        default: launch_gemm<32, 128, 1, 2, 64, 2, 3>(a, fc1, E, s); break;
     }
 }
 

@@ -82,7 +82,7 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
-def cpu_baseline(T, w, forwards):
+def cpu_baseline(T, w, forwards, min_seconds=12.0):
     import numpy as np
     import moe_inputs
     import oracle
@@ -97,15 +97,15 @@ def cpu_baseline(T, w, forwards):
     w1 = moe_inputs.bf16_bits(T["w1"])
     w2 = moe_inputs.bf16_bits(T["w2"])
     times = []
-    for i in range(forwards):
+    while len(times) < forwards or (sum(times) < min_seconds and len(times) < 20):
         t0 = time.perf_counter()
         oracle.forward(lg, x, w1, w2, w.K, w.F)
         times.append(time.perf_counter() - t0)
-        log(f"  oracle forward {i + 1}/{forwards}: {times[-1]:.2f} s")
+        log(f"  oracle forward {len(times)}: {times[-1]:.2f} s")
     med = statistics.median(times)
     return {"value": w.N / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{forwards} full forwards of the {w.name} workload (median {med:.2f} s), "
-                      f"numpy float64 with {blas} BLAS"}
+            "sample": f"{len(times)} full forwards of the {w.name} workload "
+                      f"({sum(times):.1f} s in all, median {med:.2f} s), numpy float64 with {blas} BLAS"}
 
 
 def main():
@@ -114,7 +114,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=None, help="workload name (default: the Qwen3-30B-A3B-shaped layer)")
-    ap.add_argument("--cpu-forwards", type=int, default=3, help="oracle forwards timed for cpu_baseline")
+    ap.add_argument("--cpu-forwards", type=int, default=3,
+                    help="minimum oracle forwards timed for cpu_baseline (more, up to 20, until 12 s of work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")

@@ -15,27 +15,30 @@ namespace moe {
 namespace {
 
 // ---------------------------------------------------------------------------
-// route_topk: one wavefront per token.  Each lane holds ceil(E/64) logits; K
-// rounds of a wave-wide arg-max (ties -> lower expert) pick the experts in
-// descending-logit order.  Lane k keeps round k's winner, then the K-way
-// softmax runs in float64: exp(l_k - l_0), a sum in k order that every lane
-// forms identically through shuffles, one division, one rounding to float32.
+// route_topk: a group of LPT lanes per token (16, 32 or 64, so a wave routes
+// 64/LPT tokens).  Each lane holds VPL logits (expert v*LPT + lane); K rounds
+// of a group-wide arg-max (ties -> lower expert) pick the experts in
+// descending-logit order.  Lane k of the group keeps round k's winner, then
+// the K-way softmax runs in float64: exp(l_k - l_0), a sum in k order that
+// every lane forms identically through shuffles, one division, one rounding
+// to float32.
 // ---------------------------------------------------------------------------
-constexpr int kTopkWaves = 4;
+constexpr int kTopkThreads = 256;
 
-template <int VPL>
-__global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
+template <int LPT, int VPL>
+__global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, int N, int E, int K, int* __restrict__ topk_ids,
     float* __restrict__ topk_probs) {
-    const int lane = lane_id();
-    const int t = blockIdx.x * kTopkWaves + threadIdx.x / kWave;
-    if (t >= N) return;
-    const float* row = logits + static_cast<size_t>(t) * E;
+    constexpr int TPB = kTopkThreads / LPT;   // tokens per block
+    const int g = threadIdx.x % LPT;          // lane within the token's group
+    const int t = blockIdx.x * TPB + threadIdx.x / LPT;
+    const bool live_token = t < N;            // whole groups share t, so shuffles stay in-group
+    const float* row = logits + static_cast<size_t>(live_token ? t : 0) * E;
     float v[VPL];
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
-        const int e = j * kWave + lane;
-        v[j] = e < E ? row[e] : 0.0f;
+        const int e = j * LPT + g;
+        v[j] = (live_token && e < E) ? row[e] : 0.0f;
     }
     uint32_t taken = 0;
     float my_logit = 0.0f;
@@ -45,37 +48,41 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
         int bi = INT32_MAX;   // INT32_MAX = no candidate on this lane
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
-            const int e = j * kWave + lane;
+            const int e = j * LPT + g;
             const bool live = e < E && !((taken >> j) & 1u);
             if (live && (bi == INT32_MAX || v[j] > bv)) { bv = v[j]; bi = e; }
         }
 #pragma unroll
-        for (int off = kWave / 2; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, kWave);
-            const int oi = __shfl_xor(bi, off, kWave);
+        for (int off = LPT / 2; off >= 1; off >>= 1) {
+            const float ov = __shfl_xor(bv, off, LPT);
+            const int oi = __shfl_xor(bi, off, LPT);
             const bool better = oi != INT32_MAX &&
                                 (bi == INT32_MAX || ov > bv || (ov == bv && oi < bi));
             if (better) { bv = ov; bi = oi; }
         }
-        if ((bi & (kWave - 1)) == lane) taken |= 1u << (bi / kWave);
-        if (lane == k) { my_logit = bv; my_id = bi; }
+        if (bi % LPT == g) taken |= 1u << (bi / LPT);
+        if (g == k) { my_logit = bv; my_id = bi; }
     }
-    const double top = static_cast<double>(__shfl(my_logit, 0, kWave));
-    const double ex = lane < K ? exp(static_cast<double>(my_logit) - top) : 0.0;
+    const double top = static_cast<double>(__shfl(my_logit, 0, LPT));
+    const double ex = g < K ? exp(static_cast<double>(my_logit) - top) : 0.0;
     double denom = 0.0;
-    for (int k = 0; k < K; ++k) denom += __shfl(ex, k, kWave);
-    if (lane < K) {
-        topk_ids[static_cast<size_t>(t) * K + lane] = my_id;
-        topk_probs[static_cast<size_t>(t) * K + lane] = static_cast<float>(ex / denom);
+    for (int k = 0; k < K; ++k) denom += __shfl(ex, k, LPT);
+    if (live_token && g < K) {
+        topk_ids[static_cast<size_t>(t) * K + g] = my_id;
+        topk_probs[static_cast<size_t>(t) * K + g] = static_cast<float>(ex / denom);
     }
 }
 
 // ---------------------------------------------------------------------------
 // capacity_select: one 1024-thread workgroup per expert.
 //  1. Compaction: scan topk_ids in route order (t*K + k, i.e. token order),
-//     ballot-free per-thread masks over 16 routes + a block prefix scan, and
-//     append this expert's candidates (route index, probability bits) to LDS.
-//  2. If load > C: radix-select (4 x 8-bit digits, LDS histograms) the C-th
+//     per-thread match masks over 32 routes + a block prefix scan, and append
+//     this expert's candidate route indices to LDS.  If load <= C every
+//     candidate is kept in that order and the kernel is done.
+//  2. Else gather the candidates' probabilities (bit patterns) in one batch.
+//     Up to 2048 candidates: rank each one by counting those that beat it and
+//     keep ranks < C.  Beyond that: radix-select (4 x 8-bit digits, LDS
+//     histograms) the C-th
 //     largest probability T and how many candidates equal to T still fit.
 //     Probabilities are positive floats, so their bit patterns order like
 //     their values.
@@ -84,7 +91,8 @@ __global__ __launch_bounds__(kTopkWaves * kWave) void route_topk_kernel(
 //     order.  Every route_slot entry of this expert gets exactly one write.
 // ---------------------------------------------------------------------------
 constexpr int kSelThreads = 1024;
-constexpr int kSelChunk = 16;   // routes per thread per compaction pass
+constexpr int kSelChunk = 32;   // routes per thread per compaction pass
+constexpr int kRankMax = 2048;  // rank counting up to this load, radix select above
 
 __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
     const int* __restrict__ ids, const float* __restrict__ probs, int NK, int C,
@@ -97,20 +105,22 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
     const int e = blockIdx.x;
     const int tid = threadIdx.x;
 
-    // 1. compaction
+    // 1. compaction of this expert's route indices, in route (= token) order
     int load = 0;
     for (int base = 0; base < NK; base += kSelThreads * kSelChunk) {
         const int start = base + tid * kSelChunk;
         uint32_t mask = 0;
         if (start + kSelChunk <= NK) {
             const int4* p = reinterpret_cast<const int4*>(ids + start);
+            int4 v[kSelChunk / 4];
+#pragma unroll
+            for (int q = 0; q < kSelChunk / 4; ++q) v[q] = p[q];   // all loads in flight at once
 #pragma unroll
             for (int q = 0; q < kSelChunk / 4; ++q) {
-                const int4 v = p[q];
-                mask |= (v.x == e ? 1u : 0u) << (4 * q + 0);
-                mask |= (v.y == e ? 1u : 0u) << (4 * q + 1);
-                mask |= (v.z == e ? 1u : 0u) << (4 * q + 2);
-                mask |= (v.w == e ? 1u : 0u) << (4 * q + 3);
+                mask |= (v[q].x == e ? 1u : 0u) << (4 * q + 0);
+                mask |= (v[q].y == e ? 1u : 0u) << (4 * q + 1);
+                mask |= (v[q].z == e ? 1u : 0u) << (4 * q + 2);
+                mask |= (v[q].w == e ? 1u : 0u) << (4 * q + 3);
             }
         } else {
             for (int j = 0; j < kSelChunk; ++j)
@@ -121,11 +131,7 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
         while (mask) {
             const int j = __ffs(mask) - 1;
             mask &= mask - 1;
-            const int r = start + j;
-            if (pos < kMaxN) {   // a token feeds an expert at most once, so load <= N <= kMaxN
-                s_route[pos] = static_cast<uint32_t>(r);
-                s_key[pos] = __float_as_uint(probs[r]);
-            }
+            if (pos < kMaxN) s_route[pos] = static_cast<uint32_t>(start + j);   // load <= N <= kMaxN
             ++pos;
         }
         load += total;
@@ -136,6 +142,40 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
     if (load <= C) {   // every candidate fits: slot = position in token order
         for (int i = tid; i < load; i += kSelThreads) route_slot[s_route[i]] = i;
         if (tid == 0) expert_count[e] = load;
+        return;
+    }
+    // over capacity: gather the candidates' probabilities (one batch of loads)
+    for (int i = tid; i < load; i += kSelThreads) s_key[i] = __float_as_uint(probs[s_route[i]]);
+    __syncthreads();
+
+    if (load <= kRankMax) {
+        // 2'. rank counting: candidate i is kept iff fewer than C candidates
+        // beat it (a larger key, or an equal key and a lower token, which in
+        // this token-ordered list means a lower position).  All lanes of a
+        // wave read the same key at once (an LDS broadcast), so there is no
+        // contention, unlike histogram atomics on the few exponent digits the
+        // probabilities share.  Kept flags go to bit 31 of s_route.
+        for (int i = tid; i < load; i += kSelThreads) {
+            const uint32_t ki = s_key[i];
+            int rank = 0;
+            for (int j = 0; j < load; ++j) {
+                const uint32_t kj = s_key[j];
+                rank += (kj > ki) | ((kj == ki) & (j < i));
+            }
+            if (rank < C) s_route[i] |= 0x80000000u;
+        }
+        __syncthreads();
+        const int per = (load + kSelThreads - 1) / kSelThreads;
+        const int lo = min(load, tid * per), hi = min(load, lo + per);
+        int kept = 0;
+        for (int i = lo; i < hi; ++i) kept += static_cast<int>(s_route[i] >> 31);
+        int tot = 0;
+        int slot = block_exclusive_scan(kept, s_scan, &tot);
+        for (int i = lo; i < hi; ++i) {
+            const uint32_t r = s_route[i];
+            route_slot[r & 0x7FFFFFFFu] = (r >> 31) ? slot++ : -1;
+        }
+        if (tid == 0) expert_count[e] = C;
         return;
     }
 
@@ -202,10 +242,28 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
     if (tid == 0) expert_count[e] = C;
 }
 
-template <int VPL>
+template <int LPT, int VPL>
 void launch_topk(const float* logits, int N, int E, int K, int* ids, float* probs, hipStream_t s) {
-    const int blocks = (N + kTopkWaves - 1) / kTopkWaves;
-    route_topk_kernel<VPL><<<blocks, kTopkWaves * kWave, 0, s>>>(logits, N, E, K, ids, probs);
+    constexpr int TPB = kTopkThreads / LPT;
+    const int blocks = (N + TPB - 1) / TPB;
+    route_topk_kernel<LPT, VPL><<<blocks, kTopkThreads, 0, s>>>(logits, N, E, K, ids, probs);
+}
+
+// Lanes per token: enough for K (lane k finishes route k) and for E in at
+// most 8 logits per lane when it fits, else all 64 lanes.
+void dispatch_topk(const float* logits, int N, int E, int K, int* ids, float* probs, hipStream_t s) {
+    if (K <= 16 && E <= 128) {
+        if (E <= 32) launch_topk<16, 2>(logits, N, E, K, ids, probs, s);
+        else if (E <= 64) launch_topk<16, 4>(logits, N, E, K, ids, probs, s);
+        else launch_topk<16, 8>(logits, N, E, K, ids, probs, s);
+    } else if (E <= 256) {
+        if (E <= 128) launch_topk<32, 4>(logits, N, E, K, ids, probs, s);
+        else launch_topk<32, 8>(logits, N, E, K, ids, probs, s);
+    } else if (E <= 512) {
+        launch_topk<64, 8>(logits, N, E, K, ids, probs, s);
+    } else {
+        launch_topk<64, 16>(logits, N, E, K, ids, probs, s);
+    }
 }
 
 }  // namespace
@@ -223,12 +281,7 @@ extern "C" int moe_route_capacity(const float* logits, int64_t N, int32_t E, int
         !aligned16(route_slot) || !aligned16(expert_count))
         return MOE_ERR_MISALIGNED;
     const int n = static_cast<int>(N);
-    const int vpl = (E + kWave - 1) / kWave;
-    if (vpl <= 1) launch_topk<1>(logits, n, E, K, topk_ids, topk_probs, stream);
-    else if (vpl <= 2) launch_topk<2>(logits, n, E, K, topk_ids, topk_probs, stream);
-    else if (vpl <= 4) launch_topk<4>(logits, n, E, K, topk_ids, topk_probs, stream);
-    else if (vpl <= 8) launch_topk<8>(logits, n, E, K, topk_ids, topk_probs, stream);
-    else launch_topk<16>(logits, n, E, K, topk_ids, topk_probs, stream);
+    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, stream);
     capacity_select_kernel<<<E, kSelThreads, 0, stream>>>(topk_ids, topk_probs, n * K,
                                                           static_cast<int>(C), route_slot,
                                                           expert_count);

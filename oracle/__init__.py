@@ -25,6 +25,8 @@ from .moe import (  # noqa: F401
     bf16_bits_to_f64,
     capacity_select,
     dense_forward,
+    expert_ffn,
+    f32_to_bf16_bits,
     f64_to_bf16_bits,
     forward,
     gather_combine,

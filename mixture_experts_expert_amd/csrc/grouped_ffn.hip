@@ -140,15 +140,16 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     constexpr int OUT_PITCH = OUT_COLS * 2 + 16;           // padded bf16 row of the staged output
     constexpr int RINGS = NA * A_STAGE + NB * B_STAGE;
     constexpr int LDS_BYTES = RINGS > BMT * OUT_PITCH ? RINGS : BMT * OUT_PITCH;
-    // At step kt the newest load that must have landed is A(kt) (B(kt) was
-    // issued NB-NA steps earlier).  Issued after it: B(kt+NB-NA) in the same
-    // step, then NA-2 whole steps; loads complete in issue order.
-    constexpr int WAIT = B_INST + (NA - 2) * LOADS;
+    // Step j issues A(j+NA-1) then B(j+NB-1); loads complete in issue order.
+    // Before computing slab kt, the newer of A(kt) and B(kt) must have landed:
+    // A(kt) if NA < NB (then B(kt+NB-NA) of the same step and NA-2 whole steps
+    // follow it), else B(kt) (NB-2 whole steps follow it).
+    constexpr int WAIT = NA < NB ? B_INST + (NA - 2) * LOADS : (NB - 2) * LOADS;
     static_assert(MI >= 1 && NI >= 1, "tile too small");
     static_assert(BK == 32 || BK == 64, "K slab");
     static_assert(A_INST >= 1 && B_INST >= 1 && BMT % (RPI * NW) == 0 && BNT % (RPI * NW) == 0,
                   "whole DMA blocks per wave");
-    static_assert(NA >= 2 && NB >= NA && WAIT < 64, "stage rings");
+    static_assert(NA >= 2 && NB >= 2 && WAIT < 64, "stage rings");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
@@ -264,17 +265,18 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     // ---- K loop over two LDS rings: the gathered A slabs (L2/MALL hits, short
     // latency) NA deep, the weight slabs (the HBM stream) NB deep, so NB-1
     // weight slabs are in flight while one is consumed.  Step j issues
-    // A(j+NA-1) then B(j+NB-1); the prologue replays steps -(NB-1)..-1.
+    // A(j+NA-1) then B(j+NB-1); the prologue replays the steps before 0.
     // Loads past the end of K are issued anyway (they read the next row or,
     // past the descriptor, zeros, into stages never computed) so every step
     // waits for the same count.  The barrier after the wait publishes slab kt
     // and retires slab kt-1, whose stages the new loads overwrite.
     const int KT = p.Kdim / BK;
     __syncthreads();   // the token rows are read; the rings are free
+    constexpr int LEAD = NA > NB ? NA : NB;
 #pragma unroll
-    for (int j = -(NB - 1); j < 0; ++j) {
+    for (int j = -(LEAD - 1); j < 0; ++j) {
         if (j + NA - 1 >= 0) issue_a(j + NA - 1, j + NA - 1);
-        issue_b(j + NB - 1, j + NB - 1);
+        if (j + NB - 1 >= 0) issue_b(j + NB - 1, j + NB - 1);
     }
     int abuf = 0, bbuf = 0;
     for (int kt = 0; kt < KT; ++kt) {

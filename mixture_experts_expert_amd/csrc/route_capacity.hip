@@ -25,6 +25,35 @@ namespace {
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 256;
 
+// DPP lane exchanges inside a 16-lane row (no LDS round trip).
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within each half row
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within the row
+constexpr int kDppShr1 = 0x111;       // lane i <- lane i-1 within the row
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(dpp<CTRL>(__float_as_int(v)));
+}
+template <int CTRL>
+__device__ __forceinline__ double dpp(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = dpp<CTRL>(static_cast<int>(b)), hi = dpp<CTRL>(static_cast<int>(b >> 32));
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
+}
+
+// (value, expert) arg-max step: the partner wins if its value is larger, or
+// equal with a lower expert index; INT32_MAX marks "no candidate".
+__device__ __forceinline__ void argmax_step(float& bv, int& bi, float ov, int oi) {
+    const bool better = oi != INT32_MAX && (bi == INT32_MAX || ov > bv || (ov == bv && oi < bi));
+    if (better) { bv = ov; bi = oi; }
+}
+
 template <int LPT, int VPL>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, int N, int E, int K, int* __restrict__ topk_ids,
@@ -32,7 +61,7 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     constexpr int TPB = kTopkThreads / LPT;   // tokens per block
     const int g = threadIdx.x % LPT;          // lane within the token's group
     const int t = blockIdx.x * TPB + threadIdx.x / LPT;
-    const bool live_token = t < N;            // whole groups share t, so shuffles stay in-group
+    const bool live_token = t < N;            // whole groups share t, so exchanges stay in-group
     const float* row = logits + static_cast<size_t>(live_token ? t : 0) * E;
     float v[VPL];
 #pragma unroll
@@ -45,28 +74,40 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     int my_id = 0;
     for (int k = 0; k < K; ++k) {
         float bv = 0.0f;
-        int bi = INT32_MAX;   // INT32_MAX = no candidate on this lane
+        int bi = INT32_MAX;
 #pragma unroll
         for (int j = 0; j < VPL; ++j) {
             const int e = j * LPT + g;
             const bool live = e < E && !((taken >> j) & 1u);
             if (live && (bi == INT32_MAX || v[j] > bv)) { bv = v[j]; bi = e; }
         }
+        // all-reduce over the 16-lane row with DPP, then across rows
+        argmax_step(bv, bi, dpp<kDppXor1>(bv), dpp<kDppXor1>(bi));
+        argmax_step(bv, bi, dpp<kDppXor2>(bv), dpp<kDppXor2>(bi));
+        argmax_step(bv, bi, dpp<kDppHalfMirror>(bv), dpp<kDppHalfMirror>(bi));
+        argmax_step(bv, bi, dpp<kDppMirror>(bv), dpp<kDppMirror>(bi));
 #pragma unroll
-        for (int off = LPT / 2; off >= 1; off >>= 1) {
-            const float ov = __shfl_xor(bv, off, LPT);
-            const int oi = __shfl_xor(bi, off, LPT);
-            const bool better = oi != INT32_MAX &&
-                                (bi == INT32_MAX || ov > bv || (ov == bv && oi < bi));
-            if (better) { bv = ov; bi = oi; }
-        }
+        for (int off = 16; off < LPT; off <<= 1)
+            argmax_step(bv, bi, __shfl_xor(bv, off, LPT), __shfl_xor(bi, off, LPT));
         if (bi % LPT == g) taken |= 1u << (bi / LPT);
         if (g == k) { my_logit = bv; my_id = bi; }
     }
     const double top = static_cast<double>(__shfl(my_logit, 0, LPT));
     const double ex = g < K ? exp(static_cast<double>(my_logit) - top) : 0.0;
-    double denom = 0.0;
-    for (int k = 0; k < K; ++k) denom += __shfl(ex, k, LPT);
+    // denominator: e_0 + e_1 + ... + e_{K-1} in k order.  In a 16-lane row,
+    // K-1 rounds of s <- s(lane-1) + e leave lane K-1 holding the ordered sum.
+    double denom;
+    if (LPT == 16) {
+        double s = ex;
+        for (int it = 1; it < K; ++it) {
+            const double prev = dpp<kDppShr1>(s);
+            s = g == 0 ? ex : prev + ex;
+        }
+        denom = __shfl(s, K - 1, LPT);
+    } else {
+        denom = 0.0;
+        for (int k = 0; k < K; ++k) denom += __shfl(ex, k, LPT);
+    }
     if (live_token && g < K) {
         topk_ids[static_cast<size_t>(t) * K + g] = my_id;
         topk_probs[static_cast<size_t>(t) * K + g] = static_cast<float>(ex / denom);
@@ -98,7 +139,7 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
     const int* __restrict__ ids, const float* __restrict__ probs, int NK, int C,
     int* __restrict__ route_slot, int* __restrict__ expert_count) {
     __shared__ uint32_t s_route[kMaxN];
-    __shared__ uint32_t s_key[kMaxN];
+    __shared__ __attribute__((aligned(16))) uint32_t s_key[kMaxN];
     __shared__ int s_scan[kSelThreads / kWave];
     __shared__ int s_hist[256];
     __shared__ uint32_t s_pick[2];
@@ -144,8 +185,12 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
         if (tid == 0) expert_count[e] = load;
         return;
     }
-    // over capacity: gather the candidates' probabilities (one batch of loads)
-    for (int i = tid; i < load; i += kSelThreads) s_key[i] = __float_as_uint(probs[s_route[i]]);
+    // over capacity: gather the candidates' probabilities (one batch of loads);
+    // keys past `load` up to a multiple of 16 are zero (a zero key never beats
+    // a probability, which is > 0)
+    const int padded = (load + 15) & ~15;
+    for (int i = tid; i < padded; i += kSelThreads)
+        s_key[i] = i < load ? __float_as_uint(probs[s_route[i]]) : 0u;
     __syncthreads();
 
     if (load <= kRankMax) {
@@ -158,9 +203,20 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
         for (int i = tid; i < load; i += kSelThreads) {
             const uint32_t ki = s_key[i];
             int rank = 0;
-            for (int j = 0; j < load; ++j) {
-                const uint32_t kj = s_key[j];
-                rank += (kj > ki) | ((kj == ki) & (j < i));
+            const uint4* k4 = reinterpret_cast<const uint4*>(s_key);
+            for (int j = 0; j < padded; j += 16) {   // 4 independent 16-byte reads per trip
+                uint4 q[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) q[u] = k4[j / 4 + u];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const uint32_t kk[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int jj = j + 4 * u + v;
+                        rank += (kk[v] > ki) | ((kk[v] == ki) & (jj < i));
+                    }
+                }
             }
             if (rank < C) s_route[i] |= 0x80000000u;
         }

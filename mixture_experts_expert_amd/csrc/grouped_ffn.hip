@@ -26,6 +26,7 @@
 //   * tiles are renumbered so that consecutive tiles (same expert, adjacent
 //     N-tiles, sharing the gathered A rows) land on the same XCD and its L2.
 #include <algorithm>
+#include <atomic>
 #include <initializer_list>
 
 #include "moe_common.h"
@@ -39,6 +40,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (CDNA)
+// An offset past every descriptor used here (each covers < 2 GiB): a load
+// from it returns zeros without touching memory, a store to it is dropped.
+constexpr uint32_t kOob = 0x80000000u;
 
 struct FfnArgs {
     const uint16_t* a;            // FC1: x [N, H];   FC2: act [E*Cp, I]
@@ -52,6 +56,7 @@ struct FfnArgs {
     int wrows;                    // weight rows per expert: FC1 2I, FC2 H
     int Cp;                       // slots per expert
     int MT, NT;                   // M-tiles per expert, N-tiles per expert
+    int tiles;                    // E * MT * NT
 };
 
 __device__ __forceinline__ int xcd_remap(int bid, int G) {
@@ -88,10 +93,22 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // at M0 + 16*L, so one wave fills one contiguous kilobyte.  Issued as inline
 // assembly so the compiler neither tracks it (it would otherwise wait for every
 // pending LDS-bound load before any LDS read) nor reorders it across the
-// explicit waits below ("memory" clobber).
+// explicit waits below ("memory" clobber).  The compiler's hazard checks do
+// not see into inline assembly, so the statement opens with the wait states
+// gfx9-family parts need before a vector-memory instruction: 5 after a VALU
+// write of an SGPR it reads (the descriptor may come from v_readfirstlane)
+// and 1 after a write of M0 that an LDS DMA reads.
+__device__ __forceinline__ i32x4 uniform(i32x4 r) {
+    r.x = __builtin_amdgcn_readfirstlane(r.x);
+    r.y = __builtin_amdgcn_readfirstlane(r.y);
+    r.z = __builtin_amdgcn_readfirstlane(r.z);
+    r.w = __builtin_amdgcn_readfirstlane(r.w);
+    return r;
+}
+
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(rsrc), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :: "v"(voff), "s"(uniform(rsrc)), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
                  : "memory");
 }
 
@@ -119,10 +136,20 @@ __device__ __forceinline__ uint32_t lds_off(int r, int c) {
     return static_cast<uint32_t>(r * ROWB + ((c ^ ((r / RP) % CPR)) << 4));
 }
 
+// One persistent workgroup per resident slot walks the tiles r*G + slot
+// (G workgroups, slot = the XCD-aware renumbering of its id), with one
+// continuous pair of LDS rings: the last steps of a tile already stream the
+// first K slabs of the block's next tile, so HBM keeps streaming across tile
+// boundaries and the epilogue (registers -> global, no LDS) overlaps them.
+//
+// Accumulators hold C transposed (the MFMA takes the weight fragment as its
+// first operand): a lane owns one output row (slot) and 16 output columns in
+// runs of 4, so SwiGLU pairs and the routing probability live in the lane and
+// a swap of lane halves leaves 8 consecutive bf16 columns per lane for one
+// 16-byte store.
 template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1>
 __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     constexpr int NW = WM * WN;
-    constexpr int NTHR = NW * kWave;
     constexpr int WTM = BMT / WM;
     constexpr int WTN = BNT / WN;
     constexpr int MI = WTM / 32;
@@ -136,117 +163,138 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     constexpr int A_INST = BMT / RPI / NW;                 // DMA loads per wave per stage
     constexpr int B_INST = BNT / RPI / NW;
     constexpr int LOADS = A_INST + B_INST;                 // per wave per K slab
-    constexpr int OUT_COLS = FC1 ? BNT / 2 : BNT;          // output columns of this tile
-    constexpr int OUT_PITCH = OUT_COLS * 2 + 16;           // padded bf16 row of the staged output
-    constexpr int RINGS = NA * A_STAGE + NB * B_STAGE;
-    constexpr int LDS_BYTES = RINGS > BMT * OUT_PITCH ? RINGS : BMT * OUT_PITCH;
-    // Step j issues A(j+NA-1) then B(j+NB-1); loads complete in issue order.
-    // Before computing slab kt, the newer of A(kt) and B(kt) must have landed:
-    // A(kt) if NA < NB (then B(kt+NB-NA) of the same step and NA-2 whole steps
-    // follow it), else B(kt) (NB-2 whole steps follow it).
+    constexpr int OUT_COLS = FC1 ? BNT / 2 : BNT;          // output columns of a tile
+    constexpr int STORES = FC1 ? MI * NI : 2 * MI * NI;    // 16-byte stores per lane per tile
+    constexpr int LDS_BYTES = NA * A_STAGE + NB * B_STAGE;
+    // Step j issues A(j+NA-1) then B(j+NB-1); vector-memory operations retire
+    // in issue order.  Before computing slab kt, the newer of A(kt) and B(kt)
+    // must have landed: A(kt) if NA < NB (then B(kt+NB-NA) of the same step and
+    // NA-2 whole steps follow it), else B(kt) (NB-2 whole steps follow it).  At
+    // the first step of every tile but the block's first, the previous tile's
+    // STORES epilogue stores were issued after the current slab's loads too.
     constexpr int WAIT = NA < NB ? B_INST + (NA - 2) * LOADS : (NB - 2) * LOADS;
     static_assert(MI >= 1 && NI >= 1, "tile too small");
     static_assert(BK == 32 || BK == 64, "K slab");
     static_assert(A_INST >= 1 && B_INST >= 1 && BMT % (RPI * NW) == 0 && BNT % (RPI * NW) == 0,
                   "whole DMA blocks per wave");
-    static_assert(NA >= 2 && NB >= 2 && WAIT < 64, "stage rings");
+    static_assert(NA == 2 && NB >= 2 && WAIT + STORES < 64, "stage rings");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int wm = wave / WN, wn = wave % WN;
-
-    int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int nt = logical % p.NT;
-    logical /= p.NT;
-    const int mt = logical % p.MT;
-    const int e = logical / p.MT;
-    const int m0 = mt * BMT;
-    const int64_t slot0 = static_cast<int64_t>(e) * p.Cp + m0;   // first slot of this tile
+    const int half = lane >> 5;                             // 0: lanes 0-31, 1: lanes 32-63
+    const int KT = p.Kdim / BK;                             // >= 2 (host)
+    const uint32_t row_bytes = static_cast<uint32_t>(p.Kdim) * 2u;
+    const int G = gridDim.x;
 
     // ---- DMA addressing.  Wave w's load i covers the RPI tile rows of block
     // q = w + i*NW; lane L brings row RPI*q + L/CPR, physical chunk L%CPR,
     // i.e. the logical chunk that the swizzle of that row puts there.
     const int lrow = lane / CPR;
-    auto lchunk = [&](int q) -> uint32_t {
-        const int r = RPI * q + lrow;
-        return static_cast<uint32_t>((lane % CPR) ^ ((r / (256 / ROWB)) % CPR));
+    auto dma_row = [&](int i) { return RPI * (wave + i * NW) + lrow; };
+    auto dma_chunk = [&](int i) -> uint32_t {
+        return static_cast<uint32_t>(((lane % CPR) ^ ((dma_row(i) / (256 / ROWB)) % CPR)) * 16);
     };
-    const uint32_t row_bytes = static_cast<uint32_t>(p.Kdim) * 2u;
-    i32x4 ra_rsrc, rb_rsrc;
-    if (FC1) {
-        ra_rsrc = make_rsrc(p.a, static_cast<uint32_t>(p.N) * row_bytes);
-    } else {
-        ra_rsrc = make_rsrc(p.a + static_cast<int64_t>(e) * p.Cp * p.Kdim,
-                            static_cast<uint32_t>(p.Cp) * row_bytes);
-    }
-    rb_rsrc = make_rsrc(p.w + static_cast<int64_t>(e) * p.wrows * p.Kdim,
-                        static_cast<uint32_t>(p.wrows) * row_bytes);
 
-    uint32_t a_voff[A_INST], b_voff[B_INST];
+    struct Tile {
+        int e, m0, nt;
+        i32x4 ra, rb;                 // per-expert descriptors (FC1's A: all of x)
+        uint32_t av[A_INST], bv[B_INST];
+    };
+    auto decode = [&](int t, Tile& d) {
+        d.nt = t % p.NT;
+        t /= p.NT;
+        d.m0 = (t % p.MT) * BMT;
+        d.e = t / p.MT;
+    };
+    // Weight rows (and FC2's activation rows) follow from the tile alone.
+    auto address_fixed = [&](Tile& d) {
+        d.rb = make_rsrc(p.w + static_cast<int64_t>(d.e) * p.wrows * p.Kdim,
+                         static_cast<uint32_t>(p.wrows) * row_bytes);
 #pragma unroll
-    for (int i = 0; i < A_INST; ++i) {
-        const int q = wave + i * NW;
-        const int r = RPI * q + lrow;
-        int row;
-        if (FC1) {
-            row = p.N;   // sentinel: outside the descriptor, reads zeros
-            if (m0 + r < p.Cp) {
-                const int tok = p.sorted_slot_ids[slot0 + r];
-                if (static_cast<unsigned>(tok) < static_cast<unsigned>(p.N)) row = tok;
+        for (int i = 0; i < B_INST; ++i) {
+            const int R = dma_row(i);                       // tile row
+            int wrow;
+            if (FC1) {
+                // FC1's B tile interleaves 16 gate rows and the 16 matching up
+                // rows in each 32-row MFMA block, so one accumulator block
+                // carries both.
+                const int w = R & 31;
+                wrow = (w < 16 ? 0 : p.ncols) + d.nt * (BNT / 2) + (R >> 5) * 16 + (w & 15);
+            } else {
+                wrow = d.nt * BNT + R;
             }
-        } else {
-            row = m0 + r;   // rows past Cp lie outside the expert's descriptor
+            d.bv[i] = static_cast<uint32_t>(wrow) * row_bytes + dma_chunk(i);
         }
-        a_voff[i] = static_cast<uint32_t>(row) * row_bytes + lchunk(q) * 16u;
-    }
+        if (!FC1) {
+            // rows past Cp lie outside the expert's descriptor and read zeros
+            d.ra = make_rsrc(p.a + static_cast<int64_t>(d.e) * p.Cp * p.Kdim,
+                             static_cast<uint32_t>(p.Cp) * row_bytes);
 #pragma unroll
-    for (int i = 0; i < B_INST; ++i) {
-        const int q = wave + i * NW;
-        const int R = RPI * q + lrow;                    // tile row
-        int wrow;
-        if (FC1) {
-            // FC1's B tile interleaves 16 gate rows and the 16 matching up rows
-            // in each 32-row MFMA block, so one accumulator block carries both.
-            const int w = R & 31;
-            wrow = (w < 16 ? 0 : p.ncols) + nt * (BNT / 2) + (R >> 5) * 16 + (w & 15);
-        } else {
-            wrow = nt * BNT + R;
+            for (int i = 0; i < A_INST; ++i)
+                d.av[i] = static_cast<uint32_t>(d.m0 + dma_row(i)) * row_bytes + dma_chunk(i);
         }
-        b_voff[i] = static_cast<uint32_t>(wrow) * row_bytes + lchunk(q) * 16u;
-    }
-    const uint32_t lds0 = lds_addr(smem);
-
-    auto issue_a = [&](int buf, int kt) {
-        const uint32_t koff = static_cast<uint32_t>(kt) * ROWB;
-        const uint32_t st = lds0 + buf * A_STAGE;
-#pragma unroll
-        for (int i = 0; i < A_INST; ++i) dma16(ra_rsrc, a_voff[i] + koff, st + (wave + i * NW) * 1024);
     };
-    auto issue_b = [&](int buf, int kt) {
-        const uint32_t koff = static_cast<uint32_t>(kt) * ROWB;
-        const uint32_t st = lds0 + B_RING + buf * B_STAGE;
+    // FC1's A rows are the tokens the route list names for the tile's slots.
+    auto load_tokens = [&](const Tile& d, int (&tok)[A_INST]) {
+        const int64_t slot0 = static_cast<int64_t>(d.e) * p.Cp + d.m0;
 #pragma unroll
-        for (int i = 0; i < B_INST; ++i) dma16(rb_rsrc, b_voff[i] + koff, st + (wave + i * NW) * 1024);
+        for (int i = 0; i < A_INST; ++i)
+            tok[i] = d.m0 + dma_row(i) < p.Cp ? p.sorted_slot_ids[slot0 + dma_row(i)] : p.N;
+    };
+    auto address_a = [&](Tile& d, const int (&tok)[A_INST]) {
+        d.ra = make_rsrc(p.a, static_cast<uint32_t>(p.N) * row_bytes);
+#pragma unroll
+        for (int i = 0; i < A_INST; ++i) {
+            // the sentinel row N lies outside the descriptor and reads zeros
+            const int row = static_cast<unsigned>(tok[i]) < static_cast<unsigned>(p.N) ? tok[i] : p.N;
+            d.av[i] = static_cast<uint32_t>(row) * row_bytes + dma_chunk(i);
+        }
+    };
+    // A block with no next tile still issues its look-ahead loads (so every
+    // wait counts the same operations), at an offset beyond every descriptor:
+    // they read zeros into stages that are never computed.
+    auto address_none = [&](Tile& d) {
+        d.ra = make_rsrc(p.a, 0);
+        d.rb = make_rsrc(p.w, 0);
+#pragma unroll
+        for (int i = 0; i < A_INST; ++i) d.av[i] = kOob;
+#pragma unroll
+        for (int i = 0; i < B_INST; ++i) d.bv[i] = kOob;
+    };
+
+    const uint32_t lds0 = lds_addr(smem);
+    auto issue_a = [&](const Tile& d, int stage, int kt) {
+        const uint32_t koff = static_cast<uint32_t>(kt) * ROWB;
+        const uint32_t st = lds0 + stage * A_STAGE;
+#pragma unroll
+        for (int i = 0; i < A_INST; ++i) dma16(d.ra, d.av[i] + koff, st + (wave + i * NW) * 1024);
+    };
+    auto issue_b = [&](const Tile& d, int stage, int kt) {
+        const uint32_t koff = static_cast<uint32_t>(kt) * ROWB;
+        const uint32_t st = lds0 + B_RING + stage * B_STAGE;
+#pragma unroll
+        for (int i = 0; i < B_INST; ++i) dma16(d.rb, d.bv[i] + koff, st + (wave + i * NW) * 1024);
     };
 
     floatx16 acc[MI][NI];
+    auto zero_acc = [&]() {
 #pragma unroll
-    for (int mi = 0; mi < MI; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < NI; ++ni)
+            for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
-            for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
-
+                for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
+    };
     auto compute = [&](int abuf, int bbuf) {
         const uint8_t* sA = smem + abuf * A_STAGE;
         const uint8_t* sB = smem + B_RING + bbuf * B_STAGE;
 #pragma unroll
         for (int ks = 0; ks < BK / 16; ++ks) {
-            const int c = ks * 2 + (lane >> 5);
+            const int c = ks * 2 + half;
             bf16x8 af[MI], bfr[NI];
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi)
@@ -258,107 +306,202 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
             for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
         }
     };
 
-    // ---- K loop over two LDS rings: the gathered A slabs (L2/MALL hits, short
-    // latency) NA deep, the weight slabs (the HBM stream) NB deep, so NB-1
-    // weight slabs are in flight while one is consumed.  Step j issues
-    // A(j+NA-1) then B(j+NB-1); the prologue replays the steps before 0.
-    // Loads past the end of K are issued anyway (they read the next row or,
-    // past the descriptor, zeros, into stages never computed) so every step
-    // waits for the same count.  The barrier after the wait publishes slab kt
-    // and retires slab kt-1, whose stages the new loads overwrite.
-    const int KT = p.Kdim / BK;
-    __syncthreads();   // the token rows are read; the rings are free
-    constexpr int LEAD = NA > NB ? NA : NB;
-#pragma unroll
-    for (int j = -(LEAD - 1); j < 0; ++j) {
-        if (j + NA - 1 >= 0) issue_a(j + NA - 1, j + NA - 1);
-        if (j + NB - 1 >= 0) issue_b(j + NB - 1, j + NB - 1);
+    // ---- the block's first tile and the prologue (the steps before step 0)
+    int t = xcd_remap(blockIdx.x, G);                       // < tiles: the host caps G
+    Tile cur, nxt;
+    decode(t, cur);
+    address_fixed(cur);
+    if (FC1) {
+        int tok[A_INST];
+        load_tokens(cur, tok);
+        address_a(cur, tok);
     }
-    int abuf = 0, bbuf = 0;
-    for (int kt = 0; kt < KT; ++kt) {
-        wait_vmcnt<WAIT>();
-        __syncthreads();
-        issue_a(abuf == 0 ? NA - 1 : abuf - 1, kt + NA - 1);   // stage (kt + NA - 1) % NA
-        issue_b(bbuf == 0 ? NB - 1 : bbuf - 1, kt + NB - 1);
-        compute(abuf, bbuf);
+    zero_acc();
+    int abuf = 0, bbuf = 0;                                 // stages of the slab being computed
+#pragma unroll
+    for (int j = -(NB - 1); j < 0; ++j) {                   // steps -(NB-1)..-1
+        if (j == -1) issue_a(cur, 0, 0);                    // A(0)
+        issue_b(cur, j + NB - 1, j + NB - 1);               // B(0) .. B(NB-2)
+    }
+
+    // One K step: wait for slab kt, publish it to every wave (and retire the
+    // stages of slab kt-1), refill those stages with the slabs NA-1 and NB-1
+    // ahead -- from the next tile once this one runs out -- then multiply.
+    auto refill = [&](int kt) {
+        const int ta = kt + NA - 1, tb = kt + NB - 1;
+        const int sa = abuf == 0 ? NA - 1 : abuf - 1;     // stage (kt + NA - 1) % NA
+        const int sb = bbuf == 0 ? NB - 1 : bbuf - 1;
+        if (ta < KT) issue_a(cur, sa, ta); else issue_a(nxt, sa, ta - KT);
+        if (tb < KT) issue_b(cur, sb, tb); else issue_b(nxt, sb, tb - KT);
+    };
+    auto advance = [&]() {
         abuf = abuf + 1 == NA ? 0 : abuf + 1;
         bbuf = bbuf + 1 == NB ? 0 : bbuf + 1;
-    }
-    wait_vmcnt<0>();   // no DMA may land in the LDS the epilogue reuses
-    __syncthreads();
+    };
 
-    // ---- epilogue.  32x32 accumulator layout: lane holds column (lane & 31)
-    // and rows 8*(j/4) + 4*(lane/32) + (j%4), j = 0..15.  The bf16 tile is
-    // staged in LDS (rows padded by 16 bytes) and written out in 16-byte
-    // chunks along rows.
-    const int row_lane = 4 * (lane >> 5);
-    const int col_lane = lane & 31;
-    if (FC1) {
-        // Lane l (column l&31 of a block) holds gate if (l & 16) == 0, else the
-        // up value of column l^16.  Partners swap every value and both form the
-        // activation.  (Selecting values, never vector elements, keeps the
-        // compiler from building a dynamic element index.)
-        const bool gate_lane = (lane & 16) == 0;
-        float prob[MI][16];   // routing probability of each accumulator row (0 past Cp)
+    bool first = true;
+    for (;;) {
+        const int tn = t + G;
+        const bool has_next = tn < p.tiles;
+        if (has_next) {
+            decode(tn, nxt);
+            address_fixed(nxt);
+        } else {
+            nxt.e = nxt.m0 = nxt.nt = 0;
+            address_none(nxt);
+        }
+        float prob[MI];                                     // FC1: probability of the lane's rows
+        int ntok[A_INST];
+
+        // step 0 (peeled: FC1 fetches the next tile's token rows and this
+        // tile's probabilities behind its loads, and waits for them in step 1,
+        // so no compiler-inserted wait lands on the K loop or the epilogue)
+        if (first) wait_vmcnt<WAIT>(); else wait_vmcnt<WAIT + STORES>();
+        __syncthreads();
+        refill(0);
+        if (FC1) {
+            const int64_t slot0 = static_cast<int64_t>(cur.e) * p.Cp + cur.m0;
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int row = wm * WTM + mi * 32 + 8 * (j >> 2) + row_lane + (j & 3);
-                prob[mi][j] = m0 + row < p.Cp ? p.slot_probs[slot0 + row] : 0.0f;
+            for (int mi = 0; mi < MI; ++mi) {
+                const int row = wm * WTM + mi * 32 + (lane & 31);
+                prob[mi] = cur.m0 + row < p.Cp ? p.slot_probs[slot0 + row] : 0.0f;
             }
+            if (has_next) load_tokens(nxt, ntok);
+        }
+        compute(abuf, bbuf);
+        advance();
+
+        // step 1
+        wait_vmcnt<WAIT>();
+        __syncthreads();
+        if (FC1) {
+            if (has_next) address_a(nxt, ntok);
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
+            for (int mi = 0; mi < MI; ++mi) asm volatile("" : "+v"(prob[mi]));
+        }
+        refill(1);
+        compute(abuf, bbuf);
+        advance();
+
+        for (int kt = 2; kt < KT; ++kt) {
+            wait_vmcnt<WAIT>();
+            __syncthreads();
+            refill(kt);
+            compute(abuf, bbuf);
+            advance();
+        }
+
+        // ---- epilogue: registers -> global.  Lane (row l&31, half h) holds
+        // columns 8g + 4h + (0..3) in acc[4g..4g+3].  Packed to bf16, a swap
+        // of lane halves gives lane l < 32 the columns 8g..8g+7 for even g and
+        // lane l+32 those for odd g.  Rows past Cp and columns past the output
+        // width get an offset beyond the descriptor: the store is dropped.
+        const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+            p.out + static_cast<int64_t>(cur.e) * p.Cp * p.ncols, static_cast<short>(0),
+            p.Cp * p.ncols * 2, kRsrcWord3);
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi) {
+            const int row = cur.m0 + wm * WTM + mi * 32 + (lane & 31);   // slot within the expert
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni) {
-                const int col = (wn * WTN + ni * 32) / 2 + (lane & 15);
+                if (FC1) {
+                    uint32_t x[2], y[2];
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const float mine = acc[mi][ni][j];
-                    const float other = __shfl_xor(mine, 16, kWave);
-                    const float g = gate_lane ? mine : other;
-                    const float u = gate_lane ? other : mine;
-                    const int row = wm * WTM + mi * 32 + 8 * (j >> 2) + row_lane + (j & 3);
-                    // both partners form the same value and store it to the same place
-                    *reinterpret_cast<uint16_t*>(smem + row * OUT_PITCH + col * 2) =
-                        f32_to_bf16(silu(g) * u * prob[mi][j]);
+                    for (int q = 0; q < 2; ++q) {
+                        const floatx16& v = acc[mi][ni];
+                        const float a0 = silu(v[2 * q]) * v[2 * q + 8] * prob[mi];
+                        const float a1 = silu(v[2 * q + 1]) * v[2 * q + 9] * prob[mi];
+                        const float b0 = silu(v[2 * q + 4]) * v[2 * q + 12] * prob[mi];
+                        const float b1 = silu(v[2 * q + 5]) * v[2 * q + 13] * prob[mi];
+                        x[q] = pack_bf16x2(a0, a1);
+                        y[q] = pack_bf16x2(b0, b1);
+                    }
+                    u32x4 d;
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+                    d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
+                    const int col = cur.nt * OUT_COLS + (wn * WTN + ni * 32) / 2 + 8 * half;
+                    const uint32_t off = row < p.Cp && col < p.ncols
+                        ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
+                    __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
+                } else {
+                    uint32_t g[4][2];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        g[q][0] = pack_bf16x2(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1]);
+                        g[q][1] = pack_bf16x2(acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
+                    }
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const auto s0 = __builtin_amdgcn_permlane32_swap(g[2 * q][0], g[2 * q + 1][0], false, false);
+                        const auto s1 = __builtin_amdgcn_permlane32_swap(g[2 * q][1], g[2 * q + 1][1], false, false);
+                        u32x4 d;
+                        d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
+                        const int col = cur.nt * OUT_COLS + wn * WTN + ni * 32 + 16 * q + 8 * half;
+                        const uint32_t off = row < p.Cp && col < p.ncols
+                            ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
+                        __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
+                    }
                 }
             }
-    } else {
+        }
+        zero_acc();
+        first = false;
+        if (!has_next) break;
+        t = tn;
+        cur.e = nxt.e;
+        cur.m0 = nxt.m0;
+        cur.nt = nxt.nt;
+        cur.ra = nxt.ra;
+        cur.rb = nxt.rb;
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi)
+        for (int i = 0; i < A_INST; ++i) cur.av[i] = nxt.av[i];
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                const int col = wn * WTN + ni * 32 + col_lane;
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int row = wm * WTM + mi * 32 + 8 * (j >> 2) + row_lane + (j & 3);
-                    *reinterpret_cast<uint16_t*>(smem + row * OUT_PITCH + col * 2) = f32_to_bf16(acc[mi][ni][j]);
-                }
-            }
+        for (int i = 0; i < B_INST; ++i) cur.bv[i] = nxt.bv[i];
     }
-    __syncthreads();
-    constexpr int OCPR = OUT_COLS / 8;           // 16-byte chunks per output row
-    const int col0 = nt * OUT_COLS;
-    for (int q = tid; q < BMT * OCPR; q += NTHR) {
-        const int r = q / OCPR, c = q - r * OCPR;
-        if (m0 + r < p.Cp && col0 + c * 8 < p.ncols)
-            *reinterpret_cast<u32x4*>(p.out + (slot0 + r) * p.ncols + col0 + c * 8) =
-                *reinterpret_cast<const u32x4*>(smem + r * OUT_PITCH + c * 16);
+    wait_vmcnt<0>();   // no DMA may still be writing LDS when the workgroup ends
+}
+
+// Compute units of the current device, queried once per device.
+int device_cus() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    int n = dev < 64 ? cus[dev].load(std::memory_order_relaxed) : 0;
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 1;
+        if (dev < 64) cus[dev].store(n, std::memory_order_relaxed);
     }
+    return n;
+}
+
+template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1>
+void launch_persistent(const FfnArgs& a, hipStream_t s) {
+    constexpr int threads = WM * WN * kWave;
+    auto* k = ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, FC1>;
+    static std::atomic<int> occupancy{0};   // workgroups per CU (LDS and registers decide it)
+    int occ = occupancy.load(std::memory_order_relaxed);
+    if (occ == 0) {
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void*>(k), threads, 0) !=
+                hipSuccess || occ < 1)
+            occ = 1;
+        occupancy.store(occ, std::memory_order_relaxed);
+    }
+    const int grid = std::min(a.tiles, device_cus() * occ);
+    k<<<grid, threads, 0, s>>>(a);
 }
 
 template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB>
 void launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s) {
     a.MT = (a.Cp + BMT - 1) / BMT;
     a.NT = fc1 ? (a.ncols + BNT / 2 - 1) / (BNT / 2) : (a.ncols + BNT - 1) / BNT;
-    const int grid = E * a.MT * a.NT;
-    if (fc1) ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, true><<<grid, WM * WN * kWave, 0, s>>>(a);
-    else ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, false><<<grid, WM * WN * kWave, 0, s>>>(a);
+    a.tiles = E * a.MT * a.NT;
+    if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true>(a, s);
+    else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false>(a, s);
 }
 
 // M-tile: the one (of 256, 128, 64, 32) that pads Cp the least; ties go to
@@ -373,6 +516,12 @@ int pick_tile_m(int Cp) {
 }
 
 void launch(const FfnArgs& a, bool fc1, int E, hipStream_t s) {
+    if (a.Kdim < 128) {
+        // a 64-long contraction: 32-wide K slabs, so a tile has the two
+        // steps the cross-tile look-ahead needs
+        launch_gemm<32, 128, 1, 2, 32, 2, 3>(a, fc1, E, s);
+        return;
+    }
     switch (pick_tile_m(a.Cp)) {
         // 64-wide K slabs (128 contiguous bytes per weight row per step keep the
         // HBM stream efficient); rings sized to the 160 KB LDS.

@@ -89,15 +89,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
         (const __attribute__((address_space(3))) void*)p));
 }
 
-// 16 bytes per lane from global memory straight into LDS: lane L's data lands
-// at M0 + 16*L, so one wave fills one contiguous kilobyte.  Issued as inline
-// assembly so the compiler neither tracks it (it would otherwise wait for every
-// pending LDS-bound load before any LDS read) nor reorders it across the
-// explicit waits below ("memory" clobber).  The compiler's hazard checks do
-// not see into inline assembly, so the statement opens with the wait states
-// gfx9-family parts need before a vector-memory instruction: 5 after a VALU
-// write of an SGPR it reads (the descriptor may come from v_readfirstlane)
-// and 1 after a write of M0 that an LDS DMA reads.
+// The four descriptor words as scalars (a no-op when they already are).
 __device__ __forceinline__ i32x4 uniform(i32x4 r) {
     r.x = __builtin_amdgcn_readfirstlane(r.x);
     r.y = __builtin_amdgcn_readfirstlane(r.y);
@@ -106,10 +98,26 @@ __device__ __forceinline__ i32x4 uniform(i32x4 r) {
     return r;
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane L's data lands
+// at M0 + 16*L, so one wave fills one contiguous kilobyte.  Issued as inline
+// assembly so the compiler neither tracks it (it would otherwise wait for every
+// pending LDS-bound load before any LDS read) nor reorders it across the
+// explicit waits below ("memory" clobber).  The compiler's hazard checks do
+// not see into inline assembly, so the statement opens with the wait states
+// gfx9-family parts need before a vector-memory instruction: 5 after a VALU
+// write of an SGPR it reads (the descriptor may come from v_readfirstlane)
+// and 1 after a write of M0 that an LDS DMA reads.  STREAM marks the data
+// non-temporal (read once; the caches need not keep it).
+template <bool STREAM = false>
 __device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
-    asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                 :: "v"(voff), "s"(uniform(rsrc)), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
-                 : "memory");
+    if (STREAM)
+        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                     :: "v"(voff), "s"(uniform(rsrc)), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                     : "memory");
+    else
+        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :: "v"(voff), "s"(uniform(rsrc)), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                     : "memory");
 }
 
 // Wait until at most N of this wave's vector-memory operations are pending.
@@ -201,9 +209,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
 
     struct Tile {
         int e, m0, nt;
-        i32x4 ra, rb;                 // per-expert descriptors (FC1's A: all of x)
+        i32x4 ra, rb;                 // per-expert descriptors (FC2's A and the weights)
         uint32_t av[A_INST], bv[B_INST];
     };
+    // FC1's A descriptor covers all of x, whatever the tile
+    const i32x4 x_rsrc = make_rsrc(p.a, FC1 ? static_cast<uint32_t>(p.N) * row_bytes : 0u);
     auto decode = [&](int t, Tile& d) {
         d.nt = t % p.NT;
         t /= p.NT;
@@ -246,7 +256,6 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
             tok[i] = d.m0 + dma_row(i) < p.Cp ? p.sorted_slot_ids[slot0 + dma_row(i)] : p.N;
     };
     auto address_a = [&](Tile& d, const int (&tok)[A_INST]) {
-        d.ra = make_rsrc(p.a, static_cast<uint32_t>(p.N) * row_bytes);
 #pragma unroll
         for (int i = 0; i < A_INST; ++i) {
             // the sentinel row N lies outside the descriptor and reads zeros
@@ -267,17 +276,17 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     };
 
     const uint32_t lds0 = lds_addr(smem);
-    auto issue_a = [&](const Tile& d, int stage, int kt) {
+    auto issue_a = [&](const Tile& d, int stage_off, int kt) {
         const uint32_t koff = static_cast<uint32_t>(kt) * ROWB;
-        const uint32_t st = lds0 + stage * A_STAGE;
+        const uint32_t st = lds0 + stage_off;
 #pragma unroll
-        for (int i = 0; i < A_INST; ++i) dma16(d.ra, d.av[i] + koff, st + (wave + i * NW) * 1024);
+        for (int i = 0; i < A_INST; ++i) dma16(FC1 ? x_rsrc : d.ra, d.av[i] + koff, st + (wave + i * NW) * 1024);
     };
-    auto issue_b = [&](const Tile& d, int stage, int kt) {
+    auto issue_b = [&](const Tile& d, int stage_off, int kt) {
         const uint32_t koff = static_cast<uint32_t>(kt) * ROWB;
-        const uint32_t st = lds0 + B_RING + stage * B_STAGE;
+        const uint32_t st = lds0 + B_RING + stage_off;
 #pragma unroll
-        for (int i = 0; i < B_INST; ++i) dma16(d.rb, d.bv[i] + koff, st + (wave + i * NW) * 1024);
+        for (int i = 0; i < B_INST; ++i) dma16<!FC1>(d.rb, d.bv[i] + koff, st + (wave + i * NW) * 1024);
     };
 
     floatx16 acc[MI][NI];
@@ -289,25 +298,27 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
     };
-    auto compute = [&](int abuf, int bbuf) {
-        const uint8_t* sA = smem + abuf * A_STAGE;
-        const uint8_t* sB = smem + B_RING + bbuf * B_STAGE;
+    // Byte offsets (within each ring) of the stage the current step computes
+    // and of the stage it refills -- the one the previous step computed.
+    int a_read = 0, b_read = 0;
+    int a_fill = (NA - 1) * A_STAGE, b_fill = (NB - 1) * B_STAGE;
+    auto frags = [&](int ks, bf16x8 (&af)[MI], bf16x8 (&bfr)[NI]) {
+        const uint8_t* sA = smem + a_read;
+        const uint8_t* sB = smem + B_RING + b_read;
+        const int c = ks * 2 + half;
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int c = ks * 2 + half;
-            bf16x8 af[MI], bfr[NI];
+        for (int mi = 0; mi < MI; ++mi)
+            af[mi] = *reinterpret_cast<const bf16x8*>(sA + lds_off<BK>(wm * WTM + mi * 32 + (lane & 31), c));
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-                af[mi] = *reinterpret_cast<const bf16x8*>(sA + lds_off<BK>(wm * WTM + mi * 32 + (lane & 31), c));
+        for (int ni = 0; ni < NI; ++ni)
+            bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + lds_off<BK>(wn * WTN + ni * 32 + (lane & 31), c));
+    };
+    auto mfmas = [&](const bf16x8 (&af)[MI], const bf16x8 (&bfr)[NI]) {
+#pragma unroll
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < NI; ++ni)
-                bfr[ni] = *reinterpret_cast<const bf16x8*>(sB + lds_off<BK>(wn * WTN + ni * 32 + (lane & 31), c));
-#pragma unroll
-            for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
-        }
+                acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
     };
 
     // ---- the block's first tile and the prologue (the steps before step 0)
@@ -321,26 +332,33 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         address_a(cur, tok);
     }
     zero_acc();
-    int abuf = 0, bbuf = 0;                                 // stages of the slab being computed
 #pragma unroll
     for (int j = -(NB - 1); j < 0; ++j) {                   // steps -(NB-1)..-1
         if (j == -1) issue_a(cur, 0, 0);                    // A(0)
-        issue_b(cur, j + NB - 1, j + NB - 1);               // B(0) .. B(NB-2)
+        issue_b(cur, (j + NB - 1) * B_STAGE, j + NB - 1);   // B(0) .. B(NB-2)
     }
 
-    // One K step: wait for slab kt, publish it to every wave (and retire the
-    // stages of slab kt-1), refill those stages with the slabs NA-1 and NB-1
-    // ahead -- from the next tile once this one runs out -- then multiply.
+    // One K step (after its wait and barrier, which publish slab kt and retire
+    // slab kt-1): fetch the first MFMA operands of slab kt, refill the retired
+    // stages with the slabs NA-1 and NB-1 ahead -- from the next tile once this
+    // one runs out -- while those reads are in flight, then multiply.
     auto refill = [&](int kt) {
         const int ta = kt + NA - 1, tb = kt + NB - 1;
-        const int sa = abuf == 0 ? NA - 1 : abuf - 1;     // stage (kt + NA - 1) % NA
-        const int sb = bbuf == 0 ? NB - 1 : bbuf - 1;
-        if (ta < KT) issue_a(cur, sa, ta); else issue_a(nxt, sa, ta - KT);
-        if (tb < KT) issue_b(cur, sb, tb); else issue_b(nxt, sb, tb - KT);
+        if (ta < KT) issue_a(cur, a_fill, ta); else issue_a(nxt, a_fill, ta - KT);
+        if (tb < KT) issue_b(cur, b_fill, tb); else issue_b(nxt, b_fill, tb - KT);
     };
-    auto advance = [&]() {
-        abuf = abuf + 1 == NA ? 0 : abuf + 1;
-        bbuf = bbuf + 1 == NB ? 0 : bbuf + 1;
+    auto finish = [&](bf16x8 (&af)[MI], bf16x8 (&bfr)[NI]) {
+        mfmas(af, bfr);
+#pragma unroll
+        for (int ks = 1; ks < BK / 16; ++ks) {
+            frags(ks, af, bfr);
+            mfmas(af, bfr);
+        }
+        const int a = a_read, b = b_read;
+        a_read = a + A_STAGE == NA * A_STAGE ? 0 : a + A_STAGE;
+        b_read = b + B_STAGE == NB * B_STAGE ? 0 : b + B_STAGE;
+        a_fill = a;
+        b_fill = b;
     };
 
     bool first = true;
@@ -356,12 +374,14 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         }
         float prob[MI];                                     // FC1: probability of the lane's rows
         int ntok[A_INST];
+        bf16x8 af[MI], bfr[NI];
 
         // step 0 (peeled: FC1 fetches the next tile's token rows and this
         // tile's probabilities behind its loads, and waits for them in step 1,
         // so no compiler-inserted wait lands on the K loop or the epilogue)
         if (first) wait_vmcnt<WAIT>(); else wait_vmcnt<WAIT + STORES>();
         __syncthreads();
+        frags(0, af, bfr);
         refill(0);
         if (FC1) {
             const int64_t slot0 = static_cast<int64_t>(cur.e) * p.Cp + cur.m0;
@@ -372,8 +392,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
             }
             if (has_next) load_tokens(nxt, ntok);
         }
-        compute(abuf, bbuf);
-        advance();
+        finish(af, bfr);
 
         // step 1
         wait_vmcnt<WAIT>();
@@ -383,16 +402,16 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) asm volatile("" : "+v"(prob[mi]));
         }
+        frags(0, af, bfr);
         refill(1);
-        compute(abuf, bbuf);
-        advance();
+        finish(af, bfr);
 
         for (int kt = 2; kt < KT; ++kt) {
             wait_vmcnt<WAIT>();
             __syncthreads();
+            frags(0, af, bfr);
             refill(kt);
-            compute(abuf, bbuf);
-            advance();
+            finish(af, bfr);
         }
 
         // ---- epilogue: registers -> global.  Lane (row l&31, half h) holds

@@ -196,15 +196,29 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
     if (load <= kRankMax) {
         // 2'. rank counting: candidate i is kept iff fewer than C candidates
         // beat it (a larger key, or an equal key and a lower token, which in
-        // this token-ordered list means a lower position).  All lanes of a
-        // wave read the same key at once (an LDS broadcast), so there is no
-        // contention, unlike histogram atomics on the few exponent digits the
-        // probabilities share.  Kept flags go to bit 31 of s_route.
-        for (int i = tid; i < load; i += kSelThreads) {
-            const uint32_t ki = s_key[i];
+        // this token-ordered list means a lower position).  Wave w counts, for
+        // the 64 candidates of group w % G, the beaters among the P-th part
+        // w / G of the list (G groups, P = waves / G parts), and the parts add
+        // up in LDS.  All lanes of a wave read the same key at once (an LDS
+        // broadcast), so there is no contention, unlike histogram atomics on
+        // the few exponent digits the probabilities share.  Ranks live past
+        // the keys (s_key[kRankMax..]); kept flags go to bit 31 of s_route.
+        uint32_t* s_rank = s_key + kRankMax;
+        for (int i = tid; i < load; i += kSelThreads) s_rank[i] = 0;
+        __syncthreads();
+        constexpr int kWaves = kSelThreads / kWave;
+        const int groups = (load + kWave - 1) / kWave;             // waves take turns when > kWaves
+        const int wave = tid / kWave, lane = tid % kWave;
+        for (int task = wave; task < groups * max(1, kWaves / groups); task += kWaves) {
+            const int parts = max(1, kWaves / groups);
+            const int g = task % groups, part = task / groups;
+            const int chunk = (padded / 16 + parts - 1) / parts * 16;   // keys per part
+            const int j0 = part * chunk, j1 = min(padded, j0 + chunk);
+            const int i = g * kWave + lane;
+            const uint32_t ki = i < load ? s_key[i] : 0xFFFFFFFFu;
             int rank = 0;
             const uint4* k4 = reinterpret_cast<const uint4*>(s_key);
-            for (int j = 0; j < padded; j += 16) {   // 4 independent 16-byte reads per trip
+            for (int j = j0; j < j1; j += 16) {   // 4 independent 16-byte reads per trip
                 uint4 q[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) q[u] = k4[j / 4 + u];
@@ -218,8 +232,11 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
                     }
                 }
             }
-            if (rank < C) s_route[i] |= 0x80000000u;
+            if (i < load && rank) atomicAdd(&s_rank[i], static_cast<uint32_t>(rank));
         }
+        __syncthreads();
+        for (int i = tid; i < load; i += kSelThreads)
+            if (s_rank[i] < static_cast<uint32_t>(C)) s_route[i] |= 0x80000000u;
         __syncthreads();
         const int per = (load + kSelThreads - 1) / kSelThreads;
         const int lo = min(load, tid * per), hi = min(load, lo + per);

@@ -43,6 +43,7 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (CDNA
 // An offset past every descriptor used here (each covers < 2 GiB): a load
 // from it returns zeros without touching memory, a store to it is dropped.
 constexpr uint32_t kOob = 0x80000000u;
+constexpr int kKRotate = 5;      // K slabs between the starting slabs of consecutive experts
 
 struct FfnArgs {
     const uint16_t* a;            // FC1: x [N, H];   FC2: act [E*Cp, I]
@@ -185,7 +186,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     static_assert(BK == 32 || BK == 64, "K slab");
     static_assert(A_INST >= 1 && B_INST >= 1 && BMT % (RPI * NW) == 0 && BNT % (RPI * NW) == 0,
                   "whole DMA blocks per wave");
-    static_assert(NA == 2 && NB >= 2 && WAIT + STORES < 64, "stage rings");
+    static_assert(NA >= 2 && NB >= 2 && WAIT + STORES < 64, "stage rings");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
@@ -194,7 +195,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
     const int wm = wave / WN, wn = wave % WN;
     const int half = lane >> 5;                             // 0: lanes 0-31, 1: lanes 32-63
-    const int KT = p.Kdim / BK;                             // >= 2 (host)
+    const int KT = p.Kdim / BK;                             // >= max(NA, NB - 1) (host)
     const uint32_t row_bytes = static_cast<uint32_t>(p.Kdim) * 2u;
     const int G = gridDim.x;
 
@@ -209,16 +210,27 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
 
     struct Tile {
         int e, m0, nt;
+        int rot;                      // first K slab: tiles walk K cyclically from here
         i32x4 ra, rb;                 // per-expert descriptors (FC2's A and the weights)
         uint32_t av[A_INST], bv[B_INST];
     };
     // FC1's A descriptor covers all of x, whatever the tile
     const i32x4 x_rsrc = make_rsrc(p.a, FC1 ? static_cast<uint32_t>(p.N) * row_bytes : 0u);
+    // Every expert walks its K slabs from its own starting slab.  Weight rows
+    // are often a power of two bytes apart; if every workgroup fetched the same
+    // K offset at once, all requests would share their low address bits and
+    // crowd onto few HBM channels.  The tiles of one expert keep one start so
+    // that they still share the gathered A slabs in L2.
     auto decode = [&](int t, Tile& d) {
         d.nt = t % p.NT;
         t /= p.NT;
         d.m0 = (t % p.MT) * BMT;
         d.e = t / p.MT;
+        d.rot = (d.e * kKRotate) % KT;
+    };
+    auto kslab = [&](const Tile& d, int kt) {   // the K slab a tile fetches at its step kt
+        const int k = kt + d.rot;
+        return k < KT ? k : k - KT;
     };
     // Weight rows (and FC2's activation rows) follow from the tile alone.
     auto address_fixed = [&](Tile& d) {
@@ -277,13 +289,13 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
 
     const uint32_t lds0 = lds_addr(smem);
     auto issue_a = [&](const Tile& d, int stage_off, int kt) {
-        const uint32_t koff = static_cast<uint32_t>(kt) * ROWB;
+        const uint32_t koff = static_cast<uint32_t>(kslab(d, kt)) * ROWB;
         const uint32_t st = lds0 + stage_off;
 #pragma unroll
         for (int i = 0; i < A_INST; ++i) dma16(FC1 ? x_rsrc : d.ra, d.av[i] + koff, st + (wave + i * NW) * 1024);
     };
     auto issue_b = [&](const Tile& d, int stage_off, int kt) {
-        const uint32_t koff = static_cast<uint32_t>(kt) * ROWB;
+        const uint32_t koff = static_cast<uint32_t>(kslab(d, kt)) * ROWB;
         const uint32_t st = lds0 + B_RING + stage_off;
 #pragma unroll
         for (int i = 0; i < B_INST; ++i) dma16<!FC1>(d.rb, d.bv[i] + koff, st + (wave + i * NW) * 1024);
@@ -332,27 +344,48 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         address_a(cur, tok);
     }
     zero_acc();
+    constexpr int LEAD = NA > NB ? NA : NB;
 #pragma unroll
-    for (int j = -(NB - 1); j < 0; ++j) {                   // steps -(NB-1)..-1
-        if (j == -1) issue_a(cur, 0, 0);                    // A(0)
-        issue_b(cur, (j + NB - 1) * B_STAGE, j + NB - 1);   // B(0) .. B(NB-2)
+    for (int j = -(LEAD - 1); j < 0; ++j) {                 // steps -(LEAD-1)..-1
+        if (j + NA - 1 >= 0) issue_a(cur, (j + NA - 1) * A_STAGE, j + NA - 1);   // A(0) .. A(NA-2)
+        if (j + NB - 1 >= 0) issue_b(cur, (j + NB - 1) * B_STAGE, j + NB - 1);   // B(0) .. B(NB-2)
     }
 
     // One K step (after its wait and barrier, which publish slab kt and retire
-    // slab kt-1): fetch the first MFMA operands of slab kt, refill the retired
-    // stages with the slabs NA-1 and NB-1 ahead -- from the next tile once this
-    // one runs out -- while those reads are in flight, then multiply.
-    auto refill = [&](int kt) {
+    // slab kt-1): for each 16-deep slice, fetch the MFMA operands, queue the
+    // MFMAs, then issue a share of the loads that refill the retired stages
+    // with the slabs NA-1 and NB-1 ahead (from the next tile once this one
+    // runs out).  Spreading the loads over the slices lets the memory pipe
+    // work while the matrix cores do; the issue order (all of A's loads, then
+    // all of B's) is the one the waits count on.
+    constexpr int SLICES = BK / 16;
+    auto issue_share = [&](int kt, int lo, int hi) {
         const int ta = kt + NA - 1, tb = kt + NB - 1;
-        if (ta < KT) issue_a(cur, a_fill, ta); else issue_a(nxt, a_fill, ta - KT);
-        if (tb < KT) issue_b(cur, b_fill, tb); else issue_b(nxt, b_fill, tb - KT);
-    };
-    auto finish = [&](bf16x8 (&af)[MI], bf16x8 (&bfr)[NI]) {
-        mfmas(af, bfr);
+        const bool a_cur = ta < KT, b_cur = tb < KT;
+        const uint32_t ka = static_cast<uint32_t>(a_cur ? kslab(cur, ta) : kslab(nxt, ta - KT)) * ROWB;
+        const uint32_t kb = static_cast<uint32_t>(b_cur ? kslab(cur, tb) : kslab(nxt, tb - KT)) * ROWB;
 #pragma unroll
-        for (int ks = 1; ks < BK / 16; ++ks) {
+        for (int q = 0; q < LOADS; ++q) {
+            if (q < lo || q >= hi) continue;
+            if (q < A_INST) {
+                const i32x4 r = FC1 ? x_rsrc : (a_cur ? cur.ra : nxt.ra);
+                const uint32_t v = (a_cur ? cur.av[q] : nxt.av[q]) + ka;
+                dma16(r, v, lds0 + a_fill + (wave + q * NW) * 1024);
+            } else {
+                const int i = q - A_INST;
+                const i32x4 r = b_cur ? cur.rb : nxt.rb;
+                const uint32_t v = (b_cur ? cur.bv[i] : nxt.bv[i]) + kb;
+                dma16<!FC1>(r, v, lds0 + B_RING + b_fill + (wave + i * NW) * 1024);
+            }
+        }
+    };
+    auto step = [&](int kt) {
+        bf16x8 af[MI], bfr[NI];
+#pragma unroll
+        for (int ks = 0; ks < SLICES; ++ks) {
             frags(ks, af, bfr);
             mfmas(af, bfr);
+            issue_share(kt, ks * LOADS / SLICES, (ks + 1) * LOADS / SLICES);
         }
         const int a = a_read, b = b_read;
         a_read = a + A_STAGE == NA * A_STAGE ? 0 : a + A_STAGE;
@@ -369,20 +402,18 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
             decode(tn, nxt);
             address_fixed(nxt);
         } else {
-            nxt.e = nxt.m0 = nxt.nt = 0;
+            nxt.e = nxt.m0 = nxt.nt = nxt.rot = 0;
             address_none(nxt);
         }
         float prob[MI];                                     // FC1: probability of the lane's rows
         int ntok[A_INST];
-        bf16x8 af[MI], bfr[NI];
 
-        // step 0 (peeled: FC1 fetches the next tile's token rows and this
-        // tile's probabilities behind its loads, and waits for them in step 1,
-        // so no compiler-inserted wait lands on the K loop or the epilogue)
+        // step 0 (peeled: FC1 then fetches the next tile's token rows and this
+        // tile's probabilities, and waits for them in step 1, so no
+        // compiler-inserted wait lands on the K loop or the epilogue)
         if (first) wait_vmcnt<WAIT>(); else wait_vmcnt<WAIT + STORES>();
         __syncthreads();
-        frags(0, af, bfr);
-        refill(0);
+        step(0);
         if (FC1) {
             const int64_t slot0 = static_cast<int64_t>(cur.e) * p.Cp + cur.m0;
 #pragma unroll
@@ -392,7 +423,6 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
             }
             if (has_next) load_tokens(nxt, ntok);
         }
-        finish(af, bfr);
 
         // step 1
         wait_vmcnt<WAIT>();
@@ -402,16 +432,12 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) asm volatile("" : "+v"(prob[mi]));
         }
-        frags(0, af, bfr);
-        refill(1);
-        finish(af, bfr);
+        step(1);
 
         for (int kt = 2; kt < KT; ++kt) {
             wait_vmcnt<WAIT>();
             __syncthreads();
-            frags(0, af, bfr);
-            refill(kt);
-            finish(af, bfr);
+            step(kt);
         }
 
         // ---- epilogue: registers -> global.  Lane (row l&31, half h) holds
@@ -475,6 +501,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         cur.e = nxt.e;
         cur.m0 = nxt.m0;
         cur.nt = nxt.nt;
+        cur.rot = nxt.rot;
         cur.ra = nxt.ra;
         cur.rb = nxt.rb;
 #pragma unroll
@@ -515,12 +542,15 @@ void launch_persistent(const FfnArgs& a, hipStream_t s) {
 }
 
 template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB>
-void launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s) {
+int launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s) {
+    // the cross-tile look-ahead reaches at most one tile ahead
+    if (a.Kdim % BK != 0 || a.Kdim / BK < std::max(NA, NB - 1)) return MOE_ERR_UNSUPPORTED;
     a.MT = (a.Cp + BMT - 1) / BMT;
     a.NT = fc1 ? (a.ncols + BNT / 2 - 1) / (BNT / 2) : (a.ncols + BNT - 1) / BNT;
     a.tiles = E * a.MT * a.NT;
     if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true>(a, s);
     else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false>(a, s);
+    return MOE_OK;
 }
 
 // M-tile: the one (of 256, 128, 64, 32) that pads Cp the least; ties go to
@@ -534,20 +564,19 @@ int pick_tile_m(int Cp) {
     return best;
 }
 
-void launch(const FfnArgs& a, bool fc1, int E, hipStream_t s) {
+int launch(const FfnArgs& a, bool fc1, int E, hipStream_t s) {
     if (a.Kdim < 128) {
         // a 64-long contraction: 32-wide K slabs, so a tile has the two
         // steps the cross-tile look-ahead needs
-        launch_gemm<32, 128, 1, 2, 32, 2, 3>(a, fc1, E, s);
-        return;
+        return launch_gemm<32, 128, 1, 2, 32, 2, 3>(a, fc1, E, s);
     }
     switch (pick_tile_m(a.Cp)) {
         // 64-wide K slabs (128 contiguous bytes per weight row per step keep the
         // HBM stream efficient); rings sized to the 160 KB LDS.
-        case 256: launch_gemm<256, 256, 2, 4, 64, 2, 3>(a, fc1, E, s); break;
-        case 128: launch_gemm<128, 256, 2, 4, 64, 2, 3>(a, fc1, E, s); break;
-        case 64: launch_gemm<64, 128, 2, 2, 64, 2, 3>(a, fc1, E, s); break;
-        default: launch_gemm<32, 128, 1, 2, 64, 2, 3>(a, fc1, E, s); break;
+        case 256: return launch_gemm<256, 256, 2, 4, 64, 2, 3>(a, fc1, E, s);
+        case 128: return launch_gemm<128, 256, 2, 4, 64, 2, 3>(a, fc1, E, s);
+        case 64: return launch_gemm<64, 128, 2, 2, 64, 2, 3>(a, fc1, E, s);
+        default: return launch_gemm<32, 128, 1, 2, 64, 2, 3>(a, fc1, E, s);
     }
 }
 
@@ -607,8 +636,8 @@ extern "C" int moe_grouped_fc1_swiglu(const uint16_t* x, const uint16_t* w1,
     if (N == 0 || C == 0) return MOE_OK;
     st = check_ptrs({x, w1, sorted_slot_ids, slot_probs, act});
     if (st != MOE_OK) return st;
-    launch(fc1_args(x, w1, sorted_slot_ids, slot_probs, N, H, I, Cp, act), true, E, stream);
-    return launch_status();
+    st = launch(fc1_args(x, w1, sorted_slot_ids, slot_probs, N, H, I, Cp, act), true, E, stream);
+    return st != MOE_OK ? st : launch_status();
 }
 
 extern "C" int moe_grouped_fc2(const uint16_t* act, const uint16_t* w2, int64_t N, int32_t H,
@@ -621,8 +650,8 @@ extern "C" int moe_grouped_fc2(const uint16_t* act, const uint16_t* w2, int64_t 
     if (N == 0 || C == 0) return MOE_OK;
     st = check_ptrs({act, w2, route_out});
     if (st != MOE_OK) return st;
-    launch(fc2_args(act, w2, N, H, I, Cp, route_out), false, E, stream);
-    return launch_status();
+    st = launch(fc2_args(act, w2, N, H, I, Cp, route_out), false, E, stream);
+    return st != MOE_OK ? st : launch_status();
 }
 
 extern "C" int moe_grouped_ffn_fwd(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
@@ -636,7 +665,8 @@ extern "C" int moe_grouped_ffn_fwd(const uint16_t* x, const uint16_t* w1, const 
     if (N == 0 || C == 0) return MOE_OK;
     st = check_ptrs({x, w1, w2, sorted_slot_ids, slot_probs, act, route_out});
     if (st != MOE_OK) return st;
-    launch(fc1_args(x, w1, sorted_slot_ids, slot_probs, N, H, I, Cp, act), true, E, stream);
-    launch(fc2_args(act, w2, N, H, I, Cp, route_out), false, E, stream);
-    return launch_status();
+    st = launch(fc1_args(x, w1, sorted_slot_ids, slot_probs, N, H, I, Cp, act), true, E, stream);
+    if (st != MOE_OK) return st;
+    st = launch(fc2_args(act, w2, N, H, I, Cp, route_out), false, E, stream);
+    return st != MOE_OK ? st : launch_status();
 }

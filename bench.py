@@ -1,15 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the capacity-padded, permute-free MoE FFN forward on one MI355X.
 
-One step = the whole forward (top-K routing + capacity selection, align,
-gather-in-GEMM FC1+SwiGLU, FC2, gather-combine) over one batch of seeded
+One step = the whole forward (top-K routing + capacity selection + align in
+one call, gather-in-GEMM FC1+SwiGLU, FC2, gather-combine) over one batch of seeded
 synthetic inputs already resident in HBM, replayed from one captured
 hipGraph.  Prints ONE JSON line on stdout; progress goes to stderr.
 
 Timed regions (all on the stream the library launches on):
   1. K graph replays between two HIP events -> ms_per_step, value.
   2. K eager forwards with a HIP event between consecutive C-ABI calls ->
-     average duration of each call's kernels (route+capacity, align, FC1,
+     average duration of each call's kernels (route+capacity+align, FC1,
      FC2, combine) -> TFLOP/s, GB/s and the roofline of the dominant kernel
      (FC1): HBM-bound at this shape (arithmetic intensity below the ridge).
   3. cpu_baseline: the CPU oracle on the same inputs (median of a few full
@@ -52,8 +52,10 @@ def algorithmic_bytes(w, C, Cp, kept):
     N, H, I, E, K = w.N, w.H, w.I, w.E, w.K
     R = E * Cp
     return {
-        "route_capacity": N * E * 4 + N * K * (4 + 4) + N * K * (4 + 4) + N * K * 4 + E * 4,
-        "align": N * K * 12 + E * 4 + R * 8 + (R // 32) * 4 + E * 4 + N * K * 4 + N * 4 + 4,
+        # logits in; top-K ids/probs out and back in; route_slot, counts, the
+        # route list, its inverse and the per-token counts out
+        "route_capacity_align": N * E * 4 + N * K * (4 + 4) * 2 + N * K * 4 + E * 4
+                                + R * 8 + (R // 32) * 4 + E * 4 + N * K * 4 + N * 4 + 4,
         "fc1": E * 2 * I * H * 2 + N * H * 2 + R * 8 + R * I * 2,
         "fc2": E * H * I * 2 + R * I * 2 + R * H * 2,
         "combine": kept * H * 2 + N * K * 4 + N * H * 2,
@@ -165,8 +167,7 @@ def main():
     torch.cuda.synchronize()
 
     def fwd():
-        buf.route_capacity(T["logits"])
-        buf.align()
+        buf.route_capacity_align(T["logits"])
         buf.fc1_swiglu(T["x"], T["w1"])
         buf.fc2(T["w2"])
         buf.combine()
@@ -197,8 +198,8 @@ def main():
     log(f"[bench] graph replay: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
 
     # ---- timed region 2: eager, one HIP event between consecutive calls
-    names = ["route_capacity", "align", "fc1", "fc2", "combine"]
-    calls = [lambda: buf.route_capacity(T["logits"]), buf.align,
+    names = ["route_capacity_align", "fc1", "fc2", "combine"]
+    calls = [lambda: buf.route_capacity_align(T["logits"]),
              lambda: buf.fc1_swiglu(T["x"], T["w1"]), lambda: buf.fc2(T["w2"]), buf.combine]
     tot = {n: 0.0 for n in names}
     with torch.cuda.stream(stream):

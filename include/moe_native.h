@@ -9,6 +9,9 @@
  *   moe_grouped_ffn_fwd  gather-in-GEMM FC1 -> SwiGLU*prob -> FC2 (bf16 MFMA)
  *   moe_gather_combine   each token sums its own kept, already-weighted routes
  *
+ * moe_route_capacity_align does the first two calls' work in two kernels
+ * instead of three (same outputs, bit for bit).
+ *
  * Pages defining the operations (cited by title and section):
  *   [FC] "feat(cuda-graphs): capture fixed-capacity MoE execution"
  *        (NVIDIA-NeMo Automodel pull request 2932), Design notes.
@@ -114,6 +117,19 @@ int moe_align(const int32_t* topk_ids, const float* topk_probs, const int32_t* r
               int32_t* sorted_slot_ids, float* slot_probs, int32_t* expert_ids,
               int32_t* block_start, int32_t* token_routes, int32_t* token_route_count,
               int32_t* num_tokens_post_padded, hipStream_t stream);
+
+/* Steps 1-3 in one call: moe_route_capacity followed by moe_align, with the
+ * selection workgroup of each expert writing its own segment of the route
+ * list and the token_routes entries of its routes (sources as above).  Same
+ * arguments as the two calls together, same outputs bit for bit; the
+ * per-token kept counts are accumulated with integer atomics (order-free),
+ * so the result is deterministic. */
+int moe_route_capacity_align(const float* logits, int64_t N, int32_t E, int32_t K, int64_t C,
+                             int32_t* topk_ids, float* topk_probs, int32_t* route_slot,
+                             int32_t* expert_count, int32_t* sorted_slot_ids, float* slot_probs,
+                             int32_t* expert_ids, int32_t* block_start, int32_t* token_routes,
+                             int32_t* token_route_count, int32_t* num_tokens_post_padded,
+                             hipStream_t stream);
 
 /* Step 4: permute-free grouped FFN ([PF] sections 2-3 and 6).
  *

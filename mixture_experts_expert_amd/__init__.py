@@ -19,6 +19,7 @@ from ._native import (  # noqa: F401
     moe_layout_block_m,
     moe_padded_capacity,
     moe_route_capacity,
+    moe_route_capacity_align,
     moe_source_capacity,
     moe_status_string,
 )

@@ -9,6 +9,8 @@
 //      ranks from one scan.
 #include <math.h>
 
+#include <initializer_list>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -57,7 +59,7 @@ __device__ __forceinline__ void argmax_step(float& bv, int& bi, float ov, int oi
 template <int LPT, int VPL>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, int N, int E, int K, int* __restrict__ topk_ids,
-    float* __restrict__ topk_probs) {
+    float* __restrict__ topk_probs, int* __restrict__ zero_count) {
     constexpr int TPB = kTopkThreads / LPT;   // tokens per block
     const int g = threadIdx.x % LPT;          // lane within the token's group
     const int t = blockIdx.x * TPB + threadIdx.x / LPT;
@@ -112,6 +114,8 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
         topk_ids[static_cast<size_t>(t) * K + g] = my_id;
         topk_probs[static_cast<size_t>(t) * K + g] = static_cast<float>(ex / denom);
     }
+    // the fused align counts kept routes per token with atomics: start at 0
+    if (zero_count && live_token && g == 0) zero_count[t] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -135,9 +139,57 @@ constexpr int kSelThreads = 1024;
 constexpr int kSelChunk = 32;   // routes per thread per compaction pass
 constexpr int kRankMax = 2048;  // rank counting up to this load, radix select above
 
+// Step 3's outputs, when the selection writes them itself (the fused
+// route + capacity + align call).  Expert e's workgroup owns its segment of
+// the route list and every route whose top-K pick is e, so each element has
+// exactly one writer; the per-token kept counts are the one shared output
+// (integer atomics on counters the top-K kernel zeroed).
+struct AlignOut {
+    int* sorted_slot_ids;      // null: selection only
+    float* slot_probs;
+    int* expert_ids;
+    int* block_start;
+    int* token_routes;
+    int* token_route_count;
+    int* num_tokens_post_padded;
+    int N, K, E, Cp;
+};
+
+// One candidate's outcome: route r (= t*K + k) of expert e is kept in `slot`
+// (>= 0) or dropped (-1); `prob` is its routing probability.
+__device__ __forceinline__ void emit_route(const AlignOut& ao, int e, int r, int slot, float prob) {
+    if (!ao.sorted_slot_ids) return;
+    if (slot >= 0) {
+        const int s = e * ao.Cp + slot;
+        ao.sorted_slot_ids[s] = r / ao.K;
+        ao.slot_probs[s] = prob;
+        ao.token_routes[r] = s;
+        atomicAdd(&ao.token_route_count[r / ao.K], 1);
+    } else {
+        ao.token_routes[r] = -1;
+    }
+}
+
+// The rest of expert e's segment once `kept` slots are taken: pad slots
+// (sentinel row N, probability +0), the blocks' owner, the first block, and
+// (expert 0) the padded extent.
+__device__ __forceinline__ void emit_segment(const AlignOut& ao, int e, int kept, int tid) {
+    if (!ao.sorted_slot_ids) return;
+    for (int j = kept + tid; j < ao.Cp; j += kSelThreads) {
+        ao.sorted_slot_ids[e * ao.Cp + j] = ao.N;
+        ao.slot_probs[e * ao.Cp + j] = 0.0f;
+    }
+    const int blocks = ao.Cp / kBlockM;
+    for (int b = tid; b < blocks; b += kSelThreads) ao.expert_ids[e * blocks + b] = e;
+    if (tid == 0) {
+        ao.block_start[e] = e * blocks;
+        if (e == 0) ao.num_tokens_post_padded[0] = ao.E * ao.Cp;
+    }
+}
+
 __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
     const int* __restrict__ ids, const float* __restrict__ probs, int NK, int C,
-    int* __restrict__ route_slot, int* __restrict__ expert_count) {
+    int* __restrict__ route_slot, int* __restrict__ expert_count, AlignOut ao) {
     __shared__ uint32_t s_route[kMaxN];
     __shared__ __attribute__((aligned(16))) uint32_t s_key[kMaxN];
     __shared__ int s_scan[kSelThreads / kWave];
@@ -181,7 +233,12 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
     __syncthreads();
 
     if (load <= C) {   // every candidate fits: slot = position in token order
-        for (int i = tid; i < load; i += kSelThreads) route_slot[s_route[i]] = i;
+        for (int i = tid; i < load; i += kSelThreads) {
+            const int r = static_cast<int>(s_route[i]);
+            route_slot[r] = i;
+            if (ao.sorted_slot_ids) emit_route(ao, e, r, i, probs[r]);
+        }
+        emit_segment(ao, e, load, tid);
         if (tid == 0) expert_count[e] = load;
         return;
     }
@@ -246,8 +303,11 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
         int slot = block_exclusive_scan(kept, s_scan, &tot);
         for (int i = lo; i < hi; ++i) {
             const uint32_t r = s_route[i];
-            route_slot[r & 0x7FFFFFFFu] = (r >> 31) ? slot++ : -1;
+            const int sl = (r >> 31) ? slot++ : -1;
+            route_slot[r & 0x7FFFFFFFu] = sl;
+            emit_route(ao, e, static_cast<int>(r & 0x7FFFFFFFu), sl, __uint_as_float(s_key[i]));
         }
+        emit_segment(ao, e, C, tid);
         if (tid == 0) expert_count[e] = C;
         return;
     }
@@ -310,33 +370,52 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
         const uint32_t k = s_key[i];
         bool keep = k > T;
         if (k == T) { keep = eq_seen < need; ++eq_seen; }
-        route_slot[s_route[i]] = keep ? slot++ : -1;
+        const int sl = keep ? slot++ : -1;
+        route_slot[s_route[i]] = sl;
+        emit_route(ao, e, static_cast<int>(s_route[i]), sl, __uint_as_float(k));
     }
+    emit_segment(ao, e, C, tid);
     if (tid == 0) expert_count[e] = C;
 }
 
 template <int LPT, int VPL>
-void launch_topk(const float* logits, int N, int E, int K, int* ids, float* probs, hipStream_t s) {
+void launch_topk(const float* logits, int N, int E, int K, int* ids, float* probs, int* zero_count,
+                 hipStream_t s) {
     constexpr int TPB = kTopkThreads / LPT;
     const int blocks = (N + TPB - 1) / TPB;
-    route_topk_kernel<LPT, VPL><<<blocks, kTopkThreads, 0, s>>>(logits, N, E, K, ids, probs);
+    route_topk_kernel<LPT, VPL><<<blocks, kTopkThreads, 0, s>>>(logits, N, E, K, ids, probs, zero_count);
 }
 
 // Lanes per token: enough for K (lane k finishes route k) and for E in at
 // most 8 logits per lane when it fits, else all 64 lanes.
-void dispatch_topk(const float* logits, int N, int E, int K, int* ids, float* probs, hipStream_t s) {
+void dispatch_topk(const float* logits, int N, int E, int K, int* ids, float* probs, int* zero_count,
+                   hipStream_t s) {
     if (K <= 16 && E <= 128) {
-        if (E <= 32) launch_topk<16, 2>(logits, N, E, K, ids, probs, s);
-        else if (E <= 64) launch_topk<16, 4>(logits, N, E, K, ids, probs, s);
-        else launch_topk<16, 8>(logits, N, E, K, ids, probs, s);
+        if (E <= 32) launch_topk<16, 2>(logits, N, E, K, ids, probs, zero_count, s);
+        else if (E <= 64) launch_topk<16, 4>(logits, N, E, K, ids, probs, zero_count, s);
+        else launch_topk<16, 8>(logits, N, E, K, ids, probs, zero_count, s);
     } else if (E <= 256) {
-        if (E <= 128) launch_topk<32, 4>(logits, N, E, K, ids, probs, s);
-        else launch_topk<32, 8>(logits, N, E, K, ids, probs, s);
+        if (E <= 128) launch_topk<32, 4>(logits, N, E, K, ids, probs, zero_count, s);
+        else launch_topk<32, 8>(logits, N, E, K, ids, probs, zero_count, s);
     } else if (E <= 512) {
-        launch_topk<64, 8>(logits, N, E, K, ids, probs, s);
+        launch_topk<64, 8>(logits, N, E, K, ids, probs, zero_count, s);
     } else {
-        launch_topk<64, 16>(logits, N, E, K, ids, probs, s);
+        launch_topk<64, 16>(logits, N, E, K, ids, probs, zero_count, s);
     }
+}
+
+}  // namespace
+}  // namespace moe
+
+namespace moe {
+namespace {
+
+int check_route_ptrs(std::initializer_list<const void*> ptrs) {
+    for (const void* q : ptrs) {
+        if (!q) return MOE_ERR_INVALID_ARG;
+        if (!aligned16(q)) return MOE_ERR_MISALIGNED;
+    }
+    return MOE_OK;
 }
 
 }  // namespace
@@ -349,14 +428,38 @@ extern "C" int moe_route_capacity(const float* logits, int64_t N, int32_t E, int
     int st = check_route_shape(N, E, K, C);
     if (st != MOE_OK) return st;
     if (N == 0) return MOE_OK;
-    if (!logits || !topk_ids || !topk_probs || !route_slot || !expert_count) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_probs) ||
-        !aligned16(route_slot) || !aligned16(expert_count))
-        return MOE_ERR_MISALIGNED;
+    st = check_route_ptrs({logits, topk_ids, topk_probs, route_slot, expert_count});
+    if (st != MOE_OK) return st;
     const int n = static_cast<int>(N);
-    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, stream);
+    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, nullptr, stream);
     capacity_select_kernel<<<E, kSelThreads, 0, stream>>>(topk_ids, topk_probs, n * K,
                                                           static_cast<int>(C), route_slot,
-                                                          expert_count);
+                                                          expert_count, AlignOut{});
+    return launch_status();
+}
+
+extern "C" int moe_route_capacity_align(const float* logits, int64_t N, int32_t E, int32_t K,
+                                        int64_t C, int32_t* topk_ids, float* topk_probs,
+                                        int32_t* route_slot, int32_t* expert_count,
+                                        int32_t* sorted_slot_ids, float* slot_probs,
+                                        int32_t* expert_ids, int32_t* block_start,
+                                        int32_t* token_routes, int32_t* token_route_count,
+                                        int32_t* num_tokens_post_padded, hipStream_t stream) {
+    using namespace moe;
+    int st = check_route_shape(N, E, K, C);
+    if (st != MOE_OK) return st;
+    if (N == 0) return MOE_OK;
+    st = check_route_ptrs({logits, topk_ids, topk_probs, route_slot, expert_count, sorted_slot_ids,
+                           slot_probs, expert_ids, block_start, token_routes, token_route_count,
+                           num_tokens_post_padded});
+    if (st != MOE_OK) return st;
+    const int n = static_cast<int>(N);
+    const AlignOut ao{sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
+                      token_route_count, num_tokens_post_padded, n, K, E,
+                      static_cast<int>(moe_padded_capacity(C))};
+    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, token_route_count, stream);
+    capacity_select_kernel<<<E, kSelThreads, 0, stream>>>(topk_ids, topk_probs, n * K,
+                                                          static_cast<int>(C), route_slot,
+                                                          expert_count, ao);
     return launch_status();
 }

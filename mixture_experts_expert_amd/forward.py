@@ -1,4 +1,4 @@
-"""Static-buffer MoE FFN forward over the four C-ABI calls.
+"""Static-buffer MoE FFN forward over the C-ABI calls.
 
 MoEBuffers over-allocates every intermediate to static, shape-derived
 bounds once (fixed capacity makes them exact: E*Cp slots), so the forward
@@ -48,6 +48,14 @@ class MoEBuffers:
         nat.moe_route_capacity(logits, self.K, self.C, self.topk_ids, self.topk_probs,
                                self.route_slot, self.expert_count, stream)
 
+    def route_capacity_align(self, logits, stream=None):
+        """Steps 1-3 in two launches (the selection writes the route list)."""
+        nat.moe_route_capacity_align(logits, self.K, self.C, self.topk_ids, self.topk_probs,
+                                     self.route_slot, self.expert_count, self.sorted_slot_ids,
+                                     self.slot_probs, self.expert_ids, self.block_start,
+                                     self.token_routes, self.token_route_count,
+                                     self.num_tokens_post_padded, stream)
+
     def align(self, stream=None):
         nat.moe_align(self.topk_ids, self.topk_probs, self.route_slot, self.expert_count,
                       self.N, self.E, self.K, self.C, self.sorted_slot_ids, self.slot_probs,
@@ -71,8 +79,7 @@ class MoEBuffers:
 
 def forward(buf: MoEBuffers, logits, x, w1, w2, stream=None):
     """Steps 1-5 on one stream; returns buf.y (bf16 [N, H])."""
-    buf.route_capacity(logits, stream)
-    buf.align(stream)
+    buf.route_capacity_align(logits, stream)
     buf.grouped_ffn(x, w1, w2, stream)
     buf.combine(stream)
     return buf.y

@@ -18,7 +18,8 @@ OK, INVALID, UNSUPPORTED, MISALIGNED = 0, -1, -2, -3
 def test_every_declared_symbol_is_exported():
     names = moe.header_functions()
     assert set(names) == {"moe_status_string", "moe_source_capacity", "moe_layout_block_m",
-                          "moe_padded_capacity", "moe_route_capacity", "moe_align",
+                          "moe_padded_capacity", "moe_route_capacity", "moe_route_capacity_align",
+                          "moe_align",
                           "moe_grouped_ffn_fwd", "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
                           "moe_gather_combine"}
     for n in names:
@@ -80,6 +81,16 @@ def test_route_capacity_validation():
     assert f(NUL, 16, 4, 2, 8, ALIGNED, ALIGNED, ALIGNED, ALIGNED, NUL) == INVALID
     assert f(MIS, 16, 4, 2, 8, ALIGNED, ALIGNED, ALIGNED, ALIGNED, NUL) == MISALIGNED
     assert f(NUL, 0, 4, 2, 0, NUL, NUL, NUL, NUL, NUL) == OK                                  # N = 0
+
+
+def test_route_capacity_align_validation():
+    f = lib.moe_route_capacity_align
+    o = [ALIGNED] * 7
+    assert f(ALIGNED, 16, 4, 5, 20, *([ALIGNED] * 4), *o, NUL) == INVALID                   # K > E
+    assert f(ALIGNED, 16, 2048, 8, 64, *([ALIGNED] * 4), *o, NUL) == UNSUPPORTED            # E
+    assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o[:6], MIS, NUL) == MISALIGNED
+    assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o[:2], NUL, *o[3:], NUL) == INVALID
+    assert f(NUL, 0, 4, 2, 0, *([NUL] * 4), *([NUL] * 7), NUL) == OK                         # N = 0
 
 
 def test_align_validation():

@@ -160,9 +160,11 @@ def test_gather_in_gemm_equals_pregathered_rows():
     assert torch.equal(act2, buf.act) and torch.equal(ro2, buf.route_out)
 
 
-def test_graph_capture_replay_equals_eager():
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_capture_replay_equals_eager(fused):
     """The whole forward captured once into a hipGraph, replayed on new inputs
-    written in place, with eager work between replays."""
+    written in place, with eager work between replays (separate routing and
+    align calls, or the fused routing call)."""
     w = moe_inputs.WORKLOADS["small_qwen3moe_n1024_h512_e8_k2"]
     seeds = [11, 12, 13]
     inputs = [custom_tensors(w, s) for s in seeds]
@@ -175,8 +177,11 @@ def test_graph_capture_replay_equals_eager():
     torch.cuda.current_stream().wait_stream(s)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        buf.route_capacity(static["logits"])
-        buf.align()
+        if fused:
+            buf.route_capacity_align(static["logits"])
+        else:
+            buf.route_capacity(static["logits"])
+            buf.align()
         buf.grouped_ffn(static["x"], static["w1"], static["w2"])
         buf.combine()
     for rep in range(2):
@@ -191,6 +196,46 @@ def test_graph_capture_replay_equals_eager():
             run_steps(eager, inp["logits"], inp["x"], inp["w1"], inp["w2"])
             assert torch.equal(y_graph, eager.y), f"replay {rep} differs from eager"
             assert torch.equal(slots_graph, eager.sorted_slot_ids)
+
+
+ROUTE_OUTPUTS = ("topk_ids", "topk_probs", "route_slot", "expert_count", "sorted_slot_ids",
+                 "slot_probs", "expert_ids", "block_start", "token_routes", "token_route_count",
+                 "num_tokens_post_padded")
+
+
+@pytest.mark.parametrize("case", ["tiny_n64_h64_e4_k2", "qwen3_30b_a3b_n4096_h2048_e128_k8",
+                                  "skew_zipf_n4096_e128_k8_f1.0", "skew_zipf_n4096_e128_k8_f1.5",
+                                  "tied_integer_logits", "overload_one_expert", "wide_e1000_k32",
+                                  "max_tokens_all_to_one", "ragged_n77_h192_i320"])
+def test_fused_route_align_equals_separate_calls(case, skew_alpha):
+    """moe_route_capacity_align == moe_route_capacity then moe_align, bitwise,
+    on buffers that start out filled with junk (every element is written)."""
+    if case in EDGE:
+        s, mode = EDGE[case]
+        rng = np.random.default_rng(zlib.crc32(case.encode()))
+        lg = None
+        if mode == "ties":
+            lg = rng.integers(-2, 3, size=(s.N, s.E)).astype(np.float32)
+        elif mode == "hot":
+            lg = rng.standard_normal((s.N, s.E)).astype(np.float32)
+            lg[:, 0] += 50.0
+        logits = custom_tensors(s, 17, lg)["logits"]
+    else:
+        s = moe_inputs.WORKLOADS[case]
+        logits = moe_inputs.make_tensors(s, DEV, skew_alpha=skew_alpha if s.skew else None,
+                                         weights=False)["logits"]
+    say(f"[fused routing] {case}")
+    a = MoEBuffers(s.N, s.H, s.I, s.E, s.K, s.F, DEV)
+    b = MoEBuffers(s.N, s.H, s.I, s.E, s.K, s.F, DEV)
+    for buf in (a, b):
+        for k in ROUTE_OUTPUTS:
+            getattr(buf, k).fill_(-7)
+    a.route_capacity(logits)
+    a.align()
+    b.route_capacity_align(logits)
+    torch.cuda.synchronize()
+    for k in ROUTE_OUTPUTS:
+        assert torch.equal(getattr(a, k), getattr(b, k)), k
 
 
 def test_n_zero_is_noop():

@@ -298,7 +298,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         const uint32_t koff = static_cast<uint32_t>(kslab(d, kt)) * ROWB;
         const uint32_t st = lds0 + B_RING + stage_off;
 #pragma unroll
-        for (int i = 0; i < B_INST; ++i) dma16<!FC1>(d.rb, d.bv[i] + koff, st + (wave + i * NW) * 1024);
+        for (int i = 0; i < B_INST; ++i) dma16<true>(d.rb, d.bv[i] + koff, st + (wave + i * NW) * 1024);
     };
 
     floatx16 acc[MI][NI];
@@ -375,7 +375,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
                 const int i = q - A_INST;
                 const i32x4 r = b_cur ? cur.rb : nxt.rb;
                 const uint32_t v = (b_cur ? cur.bv[i] : nxt.bv[i]) + kb;
-                dma16<!FC1>(r, v, lds0 + B_RING + b_fill + (wave + i * NW) * 1024);
+                dma16<true>(r, v, lds0 + B_RING + b_fill + (wave + i * NW) * 1024);
             }
         }
     };

@@ -253,15 +253,24 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
     if (load <= kRankMax) {
         // 2'. rank counting: candidate i is kept iff fewer than C candidates
         // beat it (a larger key, or an equal key and a lower token, which in
-        // this token-ordered list means a lower position).  Wave w counts, for
-        // the 64 candidates of group w % G, the beaters among the P-th part
-        // w / G of the list (G groups, P = waves / G parts), and the parts add
-        // up in LDS.  All lanes of a wave read the same key at once (an LDS
-        // broadcast), so there is no contention, unlike histogram atomics on
-        // the few exponent digits the probabilities share.  Ranks live past
-        // the keys (s_key[kRankMax..]); kept flags go to bit 31 of s_route.
+        // this token-ordered list means a lower position).  Both rules fold
+        // into one 64-bit key, (key << 32) | (2^32 - 1 - position): j beats i
+        // iff its 64-bit key is larger.  Wave w counts, for the 64 candidates
+        // of group w % G, the beaters among the P-th part w / G of the list
+        // (G groups, P = waves / G parts), and the parts add up in LDS.  All
+        // lanes of a wave read the same key at once (an LDS broadcast), so
+        // there is no contention, unlike histogram atomics on the few exponent
+        // digits the probabilities share.  Ranks live past the keys
+        // (s_key[kRankMax..]), the 64-bit keys past those; kept flags go to
+        // bit 31 of s_route.  Keys past `load` are zero and never beat a
+        // probability, which is > 0.
         uint32_t* s_rank = s_key + kRankMax;
-        for (int i = tid; i < load; i += kSelThreads) s_rank[i] = 0;
+        uint64_t* s_k64 = reinterpret_cast<uint64_t*>(s_key + 2 * kRankMax);
+        for (int i = tid; i < padded; i += kSelThreads) {
+            if (i < load) s_rank[i] = 0;
+            s_k64[i] = i < load ? (static_cast<uint64_t>(s_key[i]) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i))
+                                : 0ull;
+        }
         __syncthreads();
         constexpr int kWaves = kSelThreads / kWave;
         const int groups = (load + kWave - 1) / kWave;             // waves take turns when > kWaves
@@ -272,22 +281,15 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
             const int chunk = (padded / 16 + parts - 1) / parts * 16;   // keys per part
             const int j0 = part * chunk, j1 = min(padded, j0 + chunk);
             const int i = g * kWave + lane;
-            const uint32_t ki = i < load ? s_key[i] : 0xFFFFFFFFu;
+            const uint64_t ki = i < load ? s_k64[i] : ~0ull;
             int rank = 0;
-            const uint4* k4 = reinterpret_cast<const uint4*>(s_key);
-            for (int j = j0; j < j1; j += 16) {   // 4 independent 16-byte reads per trip
-                uint4 q[4];
+            const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(s_k64);
+            for (int j = j0; j < j1; j += 16) {   // 8 independent 16-byte reads per trip
+                ulonglong2 q[8];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) q[u] = k4[j / 4 + u];
+                for (int u = 0; u < 8; ++u) q[u] = k2[j / 2 + u];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const uint32_t kk[4] = {q[u].x, q[u].y, q[u].z, q[u].w};
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int jj = j + 4 * u + v;
-                        rank += (kk[v] > ki) | ((kk[v] == ki) & (jj < i));
-                    }
-                }
+                for (int u = 0; u < 8; ++u) rank += (q[u].x > ki) + (q[u].y > ki);
             }
             if (i < load && rank) atomicAdd(&s_rank[i], static_cast<uint32_t>(rank));
         }

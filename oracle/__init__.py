@@ -25,12 +25,16 @@ from .moe import (  # noqa: F401
     bf16_bits_to_f64,
     capacity_select,
     dense_forward,
+    dropless_align,
+    dropless_bound,
+    dropless_forward,
     expert_ffn,
     f32_to_bf16_bits,
     f64_to_bf16_bits,
     forward,
     gather_combine,
     grouped_ffn,
+    grouped_ffn_blocks,
     padded_capacity,
     permuted_forward,
     route_topk,

@@ -22,6 +22,12 @@ grouped_ffn           gather FC1 -> SwiGLU*prob -> FC2        library SwiGLU (E=
 gather_combine        per-token sum of its kept routes       dense path, hand-worked example
 permuted_forward      materialised-permute formulation       cross-check only
 dense_forward         per-token formulation, no capacity     cross-check only
+dropless_bound        static route-list bound, dropless      closed form
+dropless_align        dropless block-padded route list       hand-worked example, invariants,
+                                                             independent sort-based build
+grouped_ffn_blocks    FFN over a block-owned route list      = grouped_ffn on the same rows
+dropless_forward      routing -> dropless align -> FFN ->    = forward when no route drops
+                      combine
 ====================  =====================================  ==============
 
 No function here is "parity unpinned"; the FFN values are pinned only
@@ -357,3 +363,104 @@ def dense_forward(x_bits, w1_bits, w2_bits, ids, probs):
             a = silu(h[:I]) * h[I:]
             y[t] += float(probs[t, k]) * (w2 @ a)
     return y
+
+
+# ---------------------------------------------------------------------------
+# Dropless (dynamic-count) variant: every route kept, per-expert segments
+# padded to whole blocks, the real extent a device-side number
+# ---------------------------------------------------------------------------
+
+def dropless_bound(N: int, K: int, E: int, BM: int = BM_DEFAULT) -> int:
+    """Static length of the dropless route list ([PF] section 4: the route
+    list is over-allocated to T*min(topk, E) slots, and block padding adds
+    at most BM-1 slots per expert), rounded up to whole blocks."""
+    r = N * min(K, E) + E * (BM - 1)
+    return -(-r // BM) * BM
+
+
+def dropless_align(ids, probs, N: int, E: int, BM: int = BM_DEFAULT):
+    """[PF] sections 4-5 (route_list_scan, route_list_align), dropless form.
+
+    Every route is kept.  Expert e's count_e routes take consecutive slots
+    in ascending token order (their within-expert ranks), and its segment is
+    padded to a multiple of BM; segments follow each other in expert order,
+    so expert e starts at block block_start[e].  The real padded extent
+    (num_tokens_post_padded) is the sum of the padded segments.  Blocks up to
+    the extent name their expert in expert_ids; blocks past it hold -1.
+    Pad slots and the tail past the extent hold the sentinel row N with
+    probability +0.0.  token_routes[t, k] is the slot of route (t, k), and
+    every token keeps all of its K routes.
+    """
+    ids = np.asarray(ids, dtype=np.int32)
+    probs = np.asarray(probs, dtype=np.float32)
+    K = ids.shape[1]
+    R = dropless_bound(N, K, E, BM)
+    counts = np.bincount(ids.ravel(), minlength=E).astype(np.int64)[:E]
+    padded = -(-counts // BM) * BM
+    starts = np.concatenate([[0], np.cumsum(padded)[:-1]]).astype(np.int64)
+    extent = int(padded.sum())
+    sorted_slot_ids = np.full(R, N, dtype=np.int32)
+    slot_probs = np.zeros(R, dtype=np.float32)
+    token_routes = np.full((N, K), -1, dtype=np.int32)
+    route_within = np.full((N, K), -1, dtype=np.int32)
+    for e in range(E):
+        tt, kk = np.nonzero(ids == e)          # row-major: ascending token
+        s = starts[e] + np.arange(len(tt))
+        sorted_slot_ids[s] = tt
+        slot_probs[s] = probs[tt, kk]
+        token_routes[tt, kk] = s
+        route_within[tt, kk] = np.arange(len(tt))
+    expert_ids = np.full(R // BM, -1, dtype=np.int32)
+    for e in range(E):
+        expert_ids[starts[e] // BM:(starts[e] + padded[e]) // BM] = e
+    return dict(
+        R=R,
+        route_counts=counts.astype(np.int32),
+        route_within=route_within,
+        sorted_slot_ids=sorted_slot_ids,
+        slot_probs=slot_probs,
+        expert_ids=expert_ids,
+        block_start=(starts // BM).astype(np.int32),
+        token_routes=token_routes,
+        token_route_count=(token_routes >= 0).sum(axis=1).astype(np.int32),
+        num_tokens_post_padded=np.array([extent], dtype=np.int32),
+    )
+
+
+def grouped_ffn_blocks(x_bits, w1_bits, w2_bits, sorted_slot_ids, slot_probs, expert_ids,
+                       BM: int = BM_DEFAULT, experts=None):
+    """Grouped FFN over a route list whose blocks name their expert
+    ([PF] section 5: the tile -> expert map is expert_ids).  Each slot of a
+    block owned by expert e gets that expert's FFN of its gathered row
+    (zeros for the sentinel); slots of -1 blocks stay zero.  With ``experts``
+    given, only those experts' blocks are computed."""
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    N, H = x_bits.shape
+    I = np.asarray(w1_bits[0]).shape[0] // 2
+    R = len(sorted_slot_ids)
+    act = np.zeros((R, I), dtype=np.uint16)
+    route_out = np.zeros((R, H), dtype=np.uint16)
+    owner = np.repeat(np.asarray(expert_ids), BM)
+    todo = sorted(set(int(e) for e in np.unique(owner) if e >= 0))
+    for e in (todo if experts is None else [e for e in experts if e in todo]):
+        sl = np.nonzero(owner == e)[0]
+        rows = np.asarray(sorted_slot_ids)[sl]
+        a = np.zeros((len(sl), H), dtype=np.uint16)
+        real = rows < N
+        a[real] = x_bits[rows[real]]
+        act[sl], route_out[sl] = expert_ffn(a, w1_bits[e], w2_bits[e], np.asarray(slot_probs)[sl])
+    return act, route_out
+
+
+def dropless_forward(logits, x_bits, w1_bits, w2_bits, K: int, BM: int = BM_DEFAULT):
+    """Top-K routing, dropless align, grouped FFN, gather-combine."""
+    lg = np.asarray(logits, dtype=np.float32)
+    N, E = lg.shape
+    ids, probs = route_topk(lg, K)
+    meta = dropless_align(ids, probs, N, E, BM)
+    act, route_out = grouped_ffn_blocks(x_bits, w1_bits, w2_bits, meta["sorted_slot_ids"],
+                                        meta["slot_probs"], meta["expert_ids"], BM)
+    y = gather_combine(route_out, meta["token_routes"], N)
+    out = dict(topk_ids=ids, topk_probs=probs, act=act, route_out=route_out, y=y)
+    out.update(meta)
+    return out

@@ -12,6 +12,10 @@
  * moe_route_capacity_align does the first two calls' work in two kernels
  * instead of three (same outputs, bit for bit).
  *
+ * The dropless variant ([PF]'s own form: no capacity, every route kept,
+ * real extents as device scalars) runs moe_route_dropless,
+ * moe_grouped_ffn_fwd_dropless and moe_gather_combine.
+ *
  * Pages defining the operations (cited by title and section):
  *   [FC] "feat(cuda-graphs): capture fixed-capacity MoE execution"
  *        (NVIDIA-NeMo Automodel pull request 2932), Design notes.
@@ -78,6 +82,12 @@ int32_t moe_layout_block_m(void);
  * (< 0 if C < 0).  Host-only. */
 int64_t moe_padded_capacity(int64_t C);
 
+/* Dropless variant ([PF] section 4): slots of the route list when every
+ * route is kept, N*min(K,E) + E*(BM-1) rounded up to a whole block -- the
+ * static length of sorted_slot_ids, slot_probs, act and route_out; the
+ * dropless expert_ids has (this)/BM entries.  <0 on bad arguments. */
+int64_t moe_dropless_bound(int64_t N, int32_t K, int32_t E);
+
 /* Steps 1-2: top-K softmax routing and fixed-capacity drop-and-pad
  * selection ([FC] Design notes; [PF] section 4, route_counts/route_within).
  *
@@ -130,6 +140,53 @@ int moe_route_capacity_align(const float* logits, int64_t N, int32_t E, int32_t 
                              int32_t* expert_ids, int32_t* block_start, int32_t* token_routes,
                              int32_t* token_route_count, int32_t* num_tokens_post_padded,
                              hipStream_t stream);
+
+/* Dropless variant of steps 1-3 ([PF] sections 4-5: route_list_scan and
+ * route_list_align over the routing map, with no capacity): top-K routing as
+ * in moe_route_capacity, then every route is kept.
+ *
+ *   logits               in   float32 [N, E]
+ *   topk_ids, topk_probs out  [N, K]   as in moe_route_capacity
+ *   route_within         out  int32   [N, K]  rank of route (t,k) among its
+ *                                     expert's routes, in token order
+ *   route_counts         out  int32   [E]     routes per expert
+ *   sorted_slot_ids      out  int32   [Rd]    Rd = moe_dropless_bound(N, K, E).
+ *                                     Expert e's routes fill slots
+ *                                     block_start[e]*BM + rank; each expert's
+ *                                     segment is padded to a multiple of BM;
+ *                                     segments follow in expert order; pad
+ *                                     slots and the tail past the extent hold
+ *                                     the sentinel N
+ *   slot_probs           out  float32 [Rd]    probability; +0.0 at pads and tail
+ *   expert_ids           out  int32   [Rd/BM] owning expert of each block up
+ *                                     to the extent, -1 past it
+ *   block_start          out  int32   [E]     first block of each expert
+ *   token_routes         out  int32   [N, K]  slot of route (t,k) (never -1)
+ *   token_route_count    out  int32   [N]     K
+ *   num_tokens_post_padded out int32  [1]     the real extent (sum of the
+ *                                     padded segments), a device scalar
+ *
+ * Within-expert order (token order) and the pad contents follow the
+ * fixed-capacity form.  Same validation as moe_route_capacity (no C). */
+int moe_route_dropless(const float* logits, int64_t N, int32_t E, int32_t K, int32_t* topk_ids,
+                       float* topk_probs, int32_t* route_within, int32_t* route_counts,
+                       int32_t* sorted_slot_ids, float* slot_probs, int32_t* expert_ids,
+                       int32_t* block_start, int32_t* token_routes, int32_t* token_route_count,
+                       int32_t* num_tokens_post_padded, hipStream_t stream);
+
+/* Step 4 over the dropless route list: the same FC1 -> SwiGLU*prob -> FC2
+ * as moe_grouped_ffn_fwd, with expert e's rows the slots
+ * [block_start[e]*BM, block_start[e+1]*BM) (the last expert's end is
+ * num_tokens_post_padded); the tile count is taken from these device values,
+ * so nothing is read back to the host.  act [Rd, I] and route_out [Rd, H]
+ * (Rd = moe_dropless_bound(N, K, E)); rows past the extent are left
+ * unwritten and are never read by the combine.  Inputs as in
+ * moe_grouped_ffn_fwd; K only sizes Rd. */
+int moe_grouped_ffn_fwd_dropless(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                                 const int32_t* sorted_slot_ids, const float* slot_probs,
+                                 const int32_t* block_start, const int32_t* num_tokens_post_padded,
+                                 int64_t N, int32_t H, int32_t I, int32_t E, int32_t K,
+                                 uint16_t* act, uint16_t* route_out, hipStream_t stream);
 
 /* Step 4: permute-free grouped FFN ([PF] sections 2-3 and 6).
  *

@@ -12,15 +12,18 @@ from ._native import (  # noqa: F401
     header_functions,
     lib,
     moe_align,
+    moe_dropless_bound,
     moe_gather_combine,
     moe_grouped_fc1_swiglu,
     moe_grouped_fc2,
     moe_grouped_ffn_fwd,
+    moe_grouped_ffn_fwd_dropless,
     moe_layout_block_m,
     moe_padded_capacity,
     moe_route_capacity,
     moe_route_capacity_align,
+    moe_route_dropless,
     moe_source_capacity,
     moe_status_string,
 )
-from .forward import MoEBuffers, forward  # noqa: F401
+from .forward import DroplessBuffers, MoEBuffers, forward, forward_dropless  # noqa: F401

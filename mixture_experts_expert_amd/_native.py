@@ -34,6 +34,10 @@ _SIGNATURES = {
     "moe_source_capacity": (_i64, [_i64, _i32, _i32, _f64]),
     "moe_layout_block_m": (_i32, []),
     "moe_padded_capacity": (_i64, [_i64]),
+    "moe_dropless_bound": (_i64, [_i64, _i32, _i32]),
+    "moe_route_dropless": (ctypes.c_int, [_vp, _i64, _i32, _i32] + [_vp] * 12),
+    "moe_grouped_ffn_fwd_dropless": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32,
+                                                                _vp, _vp, _vp]),
     "moe_route_capacity": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp]),
     "moe_route_capacity_align": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
                                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -85,6 +89,13 @@ def moe_padded_capacity(C: int) -> int:
     if c < 0:
         raise MoEError("moe_padded_capacity", c)
     return int(c)
+
+
+def moe_dropless_bound(N: int, K: int, E: int) -> int:
+    r = lib.moe_dropless_bound(N, K, E)
+    if r < 0:
+        raise MoEError("moe_dropless_bound", r)
+    return r
 
 
 def _stream(stream):
@@ -209,3 +220,41 @@ def moe_gather_combine(route_out, token_routes, y, stream=None):
         _ptr(route_out, torch.bfloat16, R * H, "route_out"),
         _ptr(token_routes, torch.int32, N * K, "token_routes"), N, K, H, R,
         _ptr(y, torch.bfloat16, N * H, "y"), _stream(stream)))
+
+
+def moe_route_dropless(logits, K: int, topk_ids, topk_probs, route_within, route_counts,
+                       sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
+                       token_route_count, num_tokens_post_padded, stream=None):
+    N, E = logits.shape
+    R = moe_dropless_bound(N, K, E)
+    BM = moe_layout_block_m()
+    _check("moe_route_dropless", lib.moe_route_dropless(
+        _ptr(logits, torch.float32, N * E, "logits"), N, E, K,
+        _ptr(topk_ids, torch.int32, N * K, "topk_ids"),
+        _ptr(topk_probs, torch.float32, N * K, "topk_probs"),
+        _ptr(route_within, torch.int32, N * K, "route_within"),
+        _ptr(route_counts, torch.int32, E, "route_counts"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"),
+        _ptr(slot_probs, torch.float32, R, "slot_probs"),
+        _ptr(expert_ids, torch.int32, R // BM, "expert_ids"),
+        _ptr(block_start, torch.int32, E, "block_start"),
+        _ptr(token_routes, torch.int32, N * K, "token_routes"),
+        _ptr(token_route_count, torch.int32, N, "token_route_count"),
+        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"), _stream(stream)))
+
+
+def moe_grouped_ffn_fwd_dropless(x, w1, w2, sorted_slot_ids, slot_probs, block_start,
+                                 num_tokens_post_padded, K: int, act, route_out, stream=None):
+    N, H = x.shape
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    R = moe_dropless_bound(N, K, E)
+    _check("moe_grouped_ffn_fwd_dropless", lib.moe_grouped_ffn_fwd_dropless(
+        _ptr(x, torch.bfloat16, N * H, "x"), _ptr(w1, torch.bfloat16, E * 2 * I * H, "w1"),
+        _ptr(w2, torch.bfloat16, E * H * I, "w2"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"),
+        _ptr(slot_probs, torch.float32, R, "slot_probs"),
+        _ptr(block_start, torch.int32, E, "block_start"),
+        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"),
+        N, H, I, E, K, _ptr(act, torch.bfloat16, R * I, "act"),
+        _ptr(route_out, torch.bfloat16, R * H, "route_out"), _stream(stream)))

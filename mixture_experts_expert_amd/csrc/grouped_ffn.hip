@@ -57,7 +57,14 @@ struct FfnArgs {
     int wrows;                    // weight rows per expert: FC1 2I, FC2 H
     int Cp;                       // slots per expert
     int MT, NT;                   // M-tiles per expert, N-tiles per expert
-    int tiles;                    // E * MT * NT
+    int tiles;                    // E * MT * NT (fixed segments)
+    // Variable segments (the dropless route list): expert e owns the slots
+    // [block_start[e]*BM, block_start[e+1]*BM) (the last one ends at the
+    // extent); the tile count follows from these device values.
+    const int* block_start;
+    const int* extent;
+    int E;
+    int R;                        // slots of the route list (its static bound)
 };
 
 __device__ __forceinline__ int xcd_remap(int bid, int G) {
@@ -156,7 +163,7 @@ __device__ __forceinline__ uint32_t lds_off(int r, int c) {
 // runs of 4, so SwiGLU pairs and the routing probability live in the lane and
 // a swap of lane halves leaves 8 consecutive bf16 columns per lane for one
 // 16-byte store.
-template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1>
+template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1, bool DYN>
 __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BMT / WM;
@@ -210,6 +217,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
 
     struct Tile {
         int e, m0, nt;
+        int seg, len;                 // the expert's first slot and its slot count
         int rot;                      // first K slab: tiles walk K cyclically from here
         i32x4 ra, rb;                 // per-expert descriptors (FC2's A and the weights)
         uint32_t av[A_INST], bv[B_INST];
@@ -227,6 +235,42 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         d.m0 = (t % p.MT) * BMT;
         d.e = t / p.MT;
         d.rot = (d.e * kKRotate) % KT;
+        d.seg = d.e * p.Cp;
+        d.len = p.Cp;
+    };
+    // Variable segments: a cursor walks the experts (tile indices only grow
+    // within a workgroup), reading the block starts through the scalar cache.
+    typedef const __attribute__((address_space(4))) int* const_int_ptr;
+    const const_int_ptr bs = (const_int_ptr)(p.block_start);
+    // Device data is range-checked, never trusted: segments are clamped to
+    // the route list.
+    int cur_e = 0, mt_before = 0, cur_start = 0, cur_len = 0;
+    int extent_slots = 0;
+    auto segment = [&](int e) {
+        const int lo = min(max(bs[e], 0), p.R / kBlockM) * kBlockM;
+        const int hi = e + 1 < p.E ? min(max(bs[e + 1], 0), p.R / kBlockM) * kBlockM : extent_slots;
+        cur_start = lo;
+        cur_len = max(hi - lo, 0);
+    };
+    if (DYN) {
+        extent_slots = min(max(((const_int_ptr)(p.extent))[0], 0), p.R);
+        segment(0);
+    }
+    auto find = [&](int t, Tile& d) -> bool {   // DYN: tile t, or false past the last
+        const int mtile = t / p.NT;
+        while (cur_e < p.E && mtile >= mt_before + (cur_len + BMT - 1) / BMT) {
+            mt_before += (cur_len + BMT - 1) / BMT;
+            ++cur_e;
+            if (cur_e < p.E) segment(cur_e);
+        }
+        if (cur_e >= p.E) return false;
+        d.nt = t % p.NT;
+        d.e = cur_e;
+        d.m0 = (mtile - mt_before) * BMT;
+        d.rot = (d.e * kKRotate) % KT;
+        d.seg = cur_start;
+        d.len = cur_len;
+        return true;
     };
     auto kslab = [&](const Tile& d, int kt) {   // the K slab a tile fetches at its step kt
         const int k = kt + d.rot;
@@ -253,8 +297,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         }
         if (!FC1) {
             // rows past Cp lie outside the expert's descriptor and read zeros
-            d.ra = make_rsrc(p.a + static_cast<int64_t>(d.e) * p.Cp * p.Kdim,
-                             static_cast<uint32_t>(p.Cp) * row_bytes);
+            d.ra = make_rsrc(p.a + static_cast<int64_t>(d.seg) * p.Kdim,
+                             static_cast<uint32_t>(d.len) * row_bytes);
 #pragma unroll
             for (int i = 0; i < A_INST; ++i)
                 d.av[i] = static_cast<uint32_t>(d.m0 + dma_row(i)) * row_bytes + dma_chunk(i);
@@ -262,10 +306,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     };
     // FC1's A rows are the tokens the route list names for the tile's slots.
     auto load_tokens = [&](const Tile& d, int (&tok)[A_INST]) {
-        const int64_t slot0 = static_cast<int64_t>(d.e) * p.Cp + d.m0;
+        const int64_t slot0 = static_cast<int64_t>(d.seg) + d.m0;
 #pragma unroll
         for (int i = 0; i < A_INST; ++i)
-            tok[i] = d.m0 + dma_row(i) < p.Cp ? p.sorted_slot_ids[slot0 + dma_row(i)] : p.N;
+            tok[i] = d.m0 + dma_row(i) < d.len ? p.sorted_slot_ids[slot0 + dma_row(i)] : p.N;
     };
     auto address_a = [&](Tile& d, const int (&tok)[A_INST]) {
 #pragma unroll
@@ -334,9 +378,13 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     };
 
     // ---- the block's first tile and the prologue (the steps before step 0)
-    int t = xcd_remap(blockIdx.x, G);                       // < tiles: the host caps G
+    int t = xcd_remap(blockIdx.x, G);   // fixed segments: < tiles (the host caps G)
     Tile cur, nxt;
-    decode(t, cur);
+    if (DYN) {
+        if (!find(t, cur)) return;       // more workgroups than tiles: nothing to do
+    } else {
+        decode(t, cur);
+    }
     address_fixed(cur);
     if (FC1) {
         int tok[A_INST];
@@ -397,12 +445,17 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     bool first = true;
     for (;;) {
         const int tn = t + G;
-        const bool has_next = tn < p.tiles;
+        bool has_next;
+        if (DYN) {
+            has_next = find(tn, nxt);
+        } else {
+            has_next = tn < p.tiles;
+            if (has_next) decode(tn, nxt);
+        }
         if (has_next) {
-            decode(tn, nxt);
             address_fixed(nxt);
         } else {
-            nxt.e = nxt.m0 = nxt.nt = nxt.rot = 0;
+            nxt.e = nxt.m0 = nxt.nt = nxt.rot = nxt.seg = nxt.len = 0;
             address_none(nxt);
         }
         float prob[MI];                                     // FC1: probability of the lane's rows
@@ -415,11 +468,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         __syncthreads();
         step(0);
         if (FC1) {
-            const int64_t slot0 = static_cast<int64_t>(cur.e) * p.Cp + cur.m0;
+            const int64_t slot0 = static_cast<int64_t>(cur.seg) + cur.m0;
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
                 const int row = wm * WTM + mi * 32 + (lane & 31);
-                prob[mi] = cur.m0 + row < p.Cp ? p.slot_probs[slot0 + row] : 0.0f;
+                prob[mi] = cur.m0 + row < cur.len ? p.slot_probs[slot0 + row] : 0.0f;
             }
             if (has_next) load_tokens(nxt, ntok);
         }
@@ -446,8 +499,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         // lane l+32 those for odd g.  Rows past Cp and columns past the output
         // width get an offset beyond the descriptor: the store is dropped.
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-            p.out + static_cast<int64_t>(cur.e) * p.Cp * p.ncols, static_cast<short>(0),
-            p.Cp * p.ncols * 2, kRsrcWord3);
+            p.out + static_cast<int64_t>(cur.seg) * p.ncols, static_cast<short>(0),
+            cur.len * p.ncols * 2, kRsrcWord3);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
             const int row = cur.m0 + wm * WTM + mi * 32 + (lane & 31);   // slot within the expert
@@ -470,7 +523,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
                     const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
                     d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
                     const int col = cur.nt * OUT_COLS + (wn * WTN + ni * 32) / 2 + 8 * half;
-                    const uint32_t off = row < p.Cp && col < p.ncols
+                    const uint32_t off = row < cur.len && col < p.ncols
                         ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
                     __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
                 } else {
@@ -487,7 +540,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
                         u32x4 d;
                         d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
                         const int col = cur.nt * OUT_COLS + wn * WTN + ni * 32 + 16 * q + 8 * half;
-                        const uint32_t off = row < p.Cp && col < p.ncols
+                        const uint32_t off = row < cur.len && col < p.ncols
                             ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
                         __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
                     }
@@ -502,6 +555,8 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         cur.m0 = nxt.m0;
         cur.nt = nxt.nt;
         cur.rot = nxt.rot;
+        cur.seg = nxt.seg;
+        cur.len = nxt.len;
         cur.ra = nxt.ra;
         cur.rb = nxt.rb;
 #pragma unroll
@@ -525,10 +580,10 @@ int device_cus() {
     return n;
 }
 
-template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1>
+template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1, bool DYN>
 void launch_persistent(const FfnArgs& a, hipStream_t s) {
     constexpr int threads = WM * WN * kWave;
-    auto* k = ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, FC1>;
+    auto* k = ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, FC1, DYN>;
     static std::atomic<int> occupancy{0};   // workgroups per CU (LDS and registers decide it)
     int occ = occupancy.load(std::memory_order_relaxed);
     if (occ == 0) {
@@ -537,19 +592,27 @@ void launch_persistent(const FfnArgs& a, hipStream_t s) {
             occ = 1;
         occupancy.store(occ, std::memory_order_relaxed);
     }
-    const int grid = std::min(a.tiles, device_cus() * occ);
+    // variable segments: the tile count is known only on the device, so every
+    // resident slot starts and the surplus workgroups return at once
+    const int grid = DYN ? device_cus() * occ : std::min(a.tiles, device_cus() * occ);
     k<<<grid, threads, 0, s>>>(a);
 }
 
 template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB>
-int launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s) {
+int launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s, bool dyn = false) {
     // the cross-tile look-ahead reaches at most one tile ahead
     if (a.Kdim % BK != 0 || a.Kdim / BK < std::max(NA, NB - 1)) return MOE_ERR_UNSUPPORTED;
     a.MT = (a.Cp + BMT - 1) / BMT;
     a.NT = fc1 ? (a.ncols + BNT / 2 - 1) / (BNT / 2) : (a.ncols + BNT - 1) / BNT;
     a.tiles = E * a.MT * a.NT;
-    if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true>(a, s);
-    else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false>(a, s);
+    a.E = E;
+    if (dyn) {
+        if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, true>(a, s);
+        else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, true>(a, s);
+    } else {
+        if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false>(a, s);
+        else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, false>(a, s);
+    }
     return MOE_OK;
 }
 
@@ -564,19 +627,21 @@ int pick_tile_m(int Cp) {
     return best;
 }
 
-int launch(const FfnArgs& a, bool fc1, int E, hipStream_t s) {
+// rows: slots per expert (fixed segments: Cp; variable: the expected
+// padded load, which only steers the tile shape)
+int launch(const FfnArgs& a, bool fc1, int E, hipStream_t s, bool dyn = false, int rows = 0) {
     if (a.Kdim < 128) {
         // a 64-long contraction: 32-wide K slabs, so a tile has the two
         // steps the cross-tile look-ahead needs
-        return launch_gemm<32, 128, 1, 2, 32, 2, 3>(a, fc1, E, s);
+        return launch_gemm<32, 128, 1, 2, 32, 2, 3>(a, fc1, E, s, dyn);
     }
-    switch (pick_tile_m(a.Cp)) {
+    switch (pick_tile_m(dyn ? rows : a.Cp)) {
         // 64-wide K slabs (128 contiguous bytes per weight row per step keep the
         // HBM stream efficient); rings sized to the 160 KB LDS.
-        case 256: return launch_gemm<256, 256, 2, 4, 64, 2, 3>(a, fc1, E, s);
-        case 128: return launch_gemm<128, 256, 2, 4, 64, 2, 3>(a, fc1, E, s);
-        case 64: return launch_gemm<64, 128, 2, 2, 64, 2, 3>(a, fc1, E, s);
-        default: return launch_gemm<32, 128, 1, 2, 64, 2, 3>(a, fc1, E, s);
+        case 256: return launch_gemm<256, 256, 2, 4, 64, 2, 3>(a, fc1, E, s, dyn);
+        case 128: return launch_gemm<128, 256, 2, 4, 64, 2, 3>(a, fc1, E, s, dyn);
+        case 64: return launch_gemm<64, 128, 2, 2, 64, 2, 3>(a, fc1, E, s, dyn);
+        default: return launch_gemm<32, 128, 1, 2, 64, 2, 3>(a, fc1, E, s, dyn);
     }
 }
 
@@ -668,5 +733,42 @@ extern "C" int moe_grouped_ffn_fwd(const uint16_t* x, const uint16_t* w1, const 
     st = launch(fc1_args(x, w1, sorted_slot_ids, slot_probs, N, H, I, Cp, act), true, E, stream);
     if (st != MOE_OK) return st;
     st = launch(fc2_args(act, w2, N, H, I, Cp, route_out), false, E, stream);
+    return st != MOE_OK ? st : launch_status();
+}
+
+extern "C" int moe_grouped_ffn_fwd_dropless(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                                            const int32_t* sorted_slot_ids, const float* slot_probs,
+                                            const int32_t* block_start,
+                                            const int32_t* num_tokens_post_padded, int64_t N,
+                                            int32_t H, int32_t I, int32_t E, int32_t K,
+                                            uint16_t* act, uint16_t* route_out, hipStream_t stream) {
+    using namespace moe;
+    if (N < 0 || E < 1 || K < 1 || K > E) return MOE_ERR_INVALID_ARG;
+    int st = check_dims(H, I);
+    if (st != MOE_OK) return st;
+    const int64_t R = moe_dropless_bound(N, K, E);
+    if (R < 0) return static_cast<int>(R);
+    // an expert's segment holds at most N + BM - 1 slots; offsets are 32-bit
+    const int64_t big = static_cast<int64_t>(1) << 31;
+    if (R > INT32_MAX || (N + 1) * H * 2 >= big || (N + kBlockM) * std::max(H, I) * 2 >= big ||
+        static_cast<int64_t>(2) * I * H * 2 >= big)
+        return MOE_ERR_UNSUPPORTED;
+    if (N == 0) return MOE_OK;
+    st = check_ptrs({x, w1, w2, sorted_slot_ids, slot_probs, block_start, num_tokens_post_padded,
+                     act, route_out});
+    if (st != MOE_OK) return st;
+    // the tile shape follows the mean padded load per expert
+    const int rows = static_cast<int>((N * K / E + kBlockM - 1) / kBlockM * kBlockM);
+    FfnArgs a1 = fc1_args(x, w1, sorted_slot_ids, slot_probs, N, H, I, 0, act);
+    a1.block_start = block_start;
+    a1.extent = num_tokens_post_padded;
+    a1.R = static_cast<int>(R);
+    st = launch(a1, true, E, stream, true, std::max(rows, kBlockM));
+    if (st != MOE_OK) return st;
+    FfnArgs a2 = fc2_args(act, w2, N, H, I, 0, route_out);
+    a2.block_start = block_start;
+    a2.extent = num_tokens_post_padded;
+    a2.R = static_cast<int>(R);
+    st = launch(a2, false, E, stream, true, std::max(rows, kBlockM));
     return st != MOE_OK ? st : launch_status();
 }

@@ -1,3 +1,4 @@
+#include <algorithm>
 // Host-only entry points of libmoe_native: capacity arithmetic, status strings
 // and the shape checks shared by the device entry points.
 #include <cmath>
@@ -70,6 +71,13 @@ int64_t moe_padded_capacity(int64_t C) {
     if (C < 0) return MOE_ERR_INVALID_ARG;
     if (C > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     return (C + moe::kBlockM - 1) / moe::kBlockM * moe::kBlockM;
+}
+
+int64_t moe_dropless_bound(int64_t N, int32_t K, int32_t E) {
+    if (N < 0 || E < 1 || K < 1 || K > E) return MOE_ERR_INVALID_ARG;
+    if (N > moe::kMaxN || E > moe::kMaxE || K > moe::kMaxK) return MOE_ERR_UNSUPPORTED;
+    const int64_t r = N * std::min(K, E) + static_cast<int64_t>(E) * (moe::kBlockM - 1);
+    return (r + moe::kBlockM - 1) / moe::kBlockM * moe::kBlockM;
 }
 
 }  // extern "C"

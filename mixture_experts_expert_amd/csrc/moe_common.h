@@ -78,4 +78,12 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
     return base + inc - v;
 }
 
+// Dropless align launch (align.hip), shared with the routing entry point.
+int launch_align_dropless(const int32_t* topk_ids, const float* topk_probs,
+                          const int32_t* route_within, const int32_t* route_counts, int64_t N,
+                          int32_t E, int32_t K, int32_t* sorted_slot_ids, float* slot_probs,
+                          int32_t* expert_ids, int32_t* block_start, int32_t* token_routes,
+                          int32_t* token_route_count, int32_t* num_tokens_post_padded,
+                          hipStream_t stream);
+
 }  // namespace moe

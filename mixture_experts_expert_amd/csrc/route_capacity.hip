@@ -465,3 +465,31 @@ extern "C" int moe_route_capacity_align(const float* logits, int64_t N, int32_t 
                                                           expert_count, ao);
     return launch_status();
 }
+
+extern "C" int moe_route_dropless(const float* logits, int64_t N, int32_t E, int32_t K,
+                                  int32_t* topk_ids, float* topk_probs, int32_t* route_within,
+                                  int32_t* route_counts, int32_t* sorted_slot_ids,
+                                  float* slot_probs, int32_t* expert_ids, int32_t* block_start,
+                                  int32_t* token_routes, int32_t* token_route_count,
+                                  int32_t* num_tokens_post_padded, hipStream_t stream) {
+    using namespace moe;
+    int st = check_route_shape(N, E, K, N);
+    if (st != MOE_OK) return st;
+    if (moe_dropless_bound(N, K, E) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (N == 0) return MOE_OK;
+    st = check_route_ptrs({logits, topk_ids, topk_probs, route_within, route_counts,
+                           sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
+                           token_route_count, num_tokens_post_padded});
+    if (st != MOE_OK) return st;
+    const int n = static_cast<int>(N);
+    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, nullptr, stream);
+    // A capacity of N never binds (an expert gets at most one route per
+    // token): the selection pass then only ranks each expert's routes in
+    // token order and counts them.
+    capacity_select_kernel<<<E, kSelThreads, 0, stream>>>(topk_ids, topk_probs, n * K, n,
+                                                          route_within, route_counts, AlignOut{});
+    st = launch_align_dropless(topk_ids, topk_probs, route_within, route_counts, N, E, K,
+                               sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
+                               token_route_count, num_tokens_post_padded, stream);
+    return st != MOE_OK ? st : launch_status();
+}

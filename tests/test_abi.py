@@ -19,7 +19,8 @@ def test_every_declared_symbol_is_exported():
     names = moe.header_functions()
     assert set(names) == {"moe_status_string", "moe_source_capacity", "moe_layout_block_m",
                           "moe_padded_capacity", "moe_route_capacity", "moe_route_capacity_align",
-                          "moe_align",
+                          "moe_align", "moe_dropless_bound", "moe_route_dropless",
+                          "moe_grouped_ffn_fwd_dropless",
                           "moe_grouped_ffn_fwd", "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
                           "moe_gather_combine"}
     for n in names:
@@ -91,6 +92,25 @@ def test_route_capacity_align_validation():
     assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o[:6], MIS, NUL) == MISALIGNED
     assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o[:2], NUL, *o[3:], NUL) == INVALID
     assert f(NUL, 0, 4, 2, 0, *([NUL] * 4), *([NUL] * 7), NUL) == OK                         # N = 0
+
+
+def test_dropless_bound_and_validation():
+    for N, K, E in [(4, 2, 3), (4096, 8, 128), (1, 1, 1), (16384, 32, 1000), (0, 2, 4)]:
+        r = N * min(K, E) + E * 31
+        assert moe.moe_dropless_bound(N, K, E) == -(-r // 32) * 32
+    assert lib.moe_dropless_bound(4, 5, 4) == INVALID and lib.moe_dropless_bound(20000, 2, 8) == UNSUPPORTED
+    f = lib.moe_route_dropless
+    o = [ALIGNED] * 11
+    assert f(ALIGNED, 16, 4, 5, *o, NUL) == INVALID                          # K > E
+    assert f(ALIGNED, 16, 4, 2, *o[:10], MIS, NUL) == MISALIGNED
+    assert f(ALIGNED, 16, 4, 2, *o[:3], NUL, *o[4:], NUL) == INVALID
+    assert f(NUL, 0, 4, 2, *([NUL] * 11), NUL) == OK                          # N = 0
+    g = lib.moe_grouped_ffn_fwd_dropless
+    p7 = [ALIGNED] * 7
+    assert g(*p7, 16, 100, 64, 4, 2, ALIGNED, ALIGNED, NUL) == UNSUPPORTED     # H % 64
+    assert g(*p7, 16, 64, 64, 4, 5, ALIGNED, ALIGNED, NUL) == INVALID          # K > E
+    assert g(*p7, 16, 64, 64, 4, 2, ALIGNED, MIS, NUL) == MISALIGNED
+    assert g(*([NUL] * 7), 0, 64, 64, 4, 2, NUL, NUL, NUL) == OK
 
 
 def test_align_validation():

@@ -1,0 +1,146 @@
+"""GPU parity of the dropless variant (every route kept, block-padded
+segments, the real extent a device scalar) against the oracle, step-wise:
+routing bit-exact, the layout bit-exact on the GPU's own routing, the FFN
+within the bf16 tolerance on the GPU's own layout, the combine bit-exact on
+the GPU's own route_out, and y end to end."""
+
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import oracle
+from gpu_support import assert_bf16_close, check_combine_stepwise, check_routing, host, say
+from mixture_experts_expert_amd import DroplessBuffers, MoEBuffers, forward_dropless
+from test_gpu_parity import EDGE, Shape, custom_tensors
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+LAYOUT = ("route_within", "route_counts", "sorted_slot_ids", "expert_ids", "block_start",
+          "token_routes", "token_route_count", "num_tokens_post_padded")
+
+
+def run(buf, T):
+    forward_dropless(buf, T["logits"], T["x"], T["w1"], T["w2"])
+    torch.cuda.synchronize()
+
+
+def full_check(s, T, ffn=True):
+    N, H, I, E, K = s.N, s.H, s.I, s.E, s.K
+    buf = DroplessBuffers(N, H, I, E, K, DEV)
+    for k in LAYOUT + ("slot_probs",):
+        getattr(buf, k).fill_(-7)      # every element must be written
+    run(buf, T)
+    check_routing(buf, host(T["logits"]), K)
+    g_ids, g_probs = host(buf.topk_ids), host(buf.topk_probs)
+    m = oracle.dropless_align(g_ids, g_probs, N, E, buf.BM)
+    assert m["R"] == buf.R
+    for k in LAYOUT:
+        assert np.array_equal(host(getattr(buf, k)).reshape(m[k].shape), m[k]), f"{k} differs"
+    assert np.array_equal(host(buf.slot_probs).view(np.uint32), m["slot_probs"].view(np.uint32))
+    ext = int(m["num_tokens_post_padded"][0])
+    say(f"  extent={ext}/{buf.R} pads={int((m['sorted_slot_ids'][:ext] == N).sum())}")
+    if ffn:
+        x, w1, w2 = host(T["x"]), host(T["w1"]), host(T["w2"])
+        act, ro = oracle.grouped_ffn_blocks(x, w1, w2, m["sorted_slot_ids"], m["slot_probs"],
+                                            m["expert_ids"], buf.BM)
+        assert_bf16_close(host(buf.act)[:ext], act[:ext], "act")
+        assert_bf16_close(host(buf.route_out)[:ext], ro[:ext], "route_out")
+        pads = m["sorted_slot_ids"][:ext] == N
+        assert np.all(host(buf.route_out)[:ext][pads] == 0), "pad rows must be zero"
+        check_combine_stepwise(buf, N)
+        assert_bf16_close(host(buf.y), oracle.gather_combine(ro, m["token_routes"], N),
+                          "y (end to end)")
+    return buf, m
+
+
+@pytest.mark.parametrize("name", ["tiny_n64_h64_e4_k2", "small_qwen3moe_n1024_h512_e8_k2",
+                                  "qwen3_30b_a3b_n4096_h2048_e128_k8",
+                                  "skew_zipf_n4096_e128_k8_f1.0"])
+def test_dropless_workload_parity(name, skew_alpha):
+    w = moe_inputs.WORKLOADS[name]
+    say(f"[dropless] {name}")
+    T = moe_inputs.make_tensors(w, DEV, skew_alpha=skew_alpha if w.skew else None)
+    full_check(w, T)
+
+
+@pytest.mark.parametrize("case", ["single_token", "ragged_n77_h192_i320", "tied_integer_logits",
+                                  "overload_one_expert", "wide_e1000_k32", "e100_k7_f2",
+                                  "max_tokens_all_to_one"])
+def test_dropless_edge_case_parity(case):
+    s, mode = EDGE[case]
+    say(f"[dropless edge] {case}")
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    lg = None
+    if mode == "ties":
+        lg = rng.integers(-2, 3, size=(s.N, s.E)).astype(np.float32)
+    elif mode == "hot":
+        lg = rng.standard_normal((s.N, s.E)).astype(np.float32)
+        lg[:, 0] += 50.0
+    T = custom_tensors(s, 17, lg)
+    buf, m = full_check(s, T)
+    if mode == "hot":
+        assert int(m["route_counts"][0]) == s.N      # every token routed to expert 0, all kept
+
+
+def test_dropless_equals_capacity_path_without_drops():
+    """With a capacity that binds nowhere (F = E/K), the fixed-capacity path
+    keeps every route too; per-route arithmetic is the same, so y is equal
+    bit for bit although the slot layouts differ."""
+    w = moe_inputs.WORKLOADS["small_qwen3moe_n1024_h512_e8_k2"]
+    T = moe_inputs.make_tensors(w, DEV)
+    d = DroplessBuffers(w.N, w.H, w.I, w.E, w.K, DEV)
+    run(d, T)
+    c = MoEBuffers(w.N, w.H, w.I, w.E, w.K, w.E / w.K, DEV)
+    c.route_capacity_align(T["logits"])
+    c.grouped_ffn(T["x"], T["w1"], T["w2"])
+    c.combine()
+    torch.cuda.synchronize()
+    assert int((c.token_routes < 0).sum()) == 0
+    assert torch.equal(d.y, c.y)
+
+
+def test_dropless_graph_replay_equals_eager():
+    """Captured once, replayed on new logits and activations written in
+    place: the real extents change with the routing, and only device
+    scalars carry them."""
+    w = moe_inputs.WORKLOADS["small_qwen3moe_n1024_h512_e8_k2"]
+    inputs = [custom_tensors(w, s) for s in (21, 22, 23)]
+    skewed = inputs[2]["logits"].clone()
+    skewed[:, 0] += 3.0                                 # a different extent and owner map
+    inputs[2]["logits"] = skewed
+    static = {k: v.clone() for k, v in inputs[0].items()}
+    buf = DroplessBuffers(w.N, w.H, w.I, w.E, w.K, DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run(buf, static)
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        forward_dropless(buf, static["logits"], static["x"], static["w1"], static["w2"])
+    extents = set()
+    for rep in range(2):
+        for inp in inputs:
+            for k in static:
+                static[k].copy_(inp[k])
+            g.replay()
+            torch.cuda.synchronize()
+            eager = DroplessBuffers(w.N, w.H, w.I, w.E, w.K, DEV)
+            run(eager, inp)
+            assert torch.equal(buf.y, eager.y), f"replay {rep} differs from eager"
+            assert torch.equal(buf.sorted_slot_ids, eager.sorted_slot_ids)
+            extents.add(int(eager.num_tokens_post_padded.item()))
+    assert len(extents) > 1, "the inputs should give different extents"
+
+
+def test_dropless_n_zero_is_noop():
+    buf = DroplessBuffers(0, 64, 64, 4, 2, DEV)
+    T = {"logits": torch.zeros(0, 4, device=DEV), "x": torch.zeros(0, 64, dtype=torch.bfloat16, device=DEV),
+         "w1": torch.zeros(4, 128, 64, dtype=torch.bfloat16, device=DEV),
+         "w2": torch.zeros(4, 64, 64, dtype=torch.bfloat16, device=DEV)}
+    run(buf, T)
+    assert buf.y.numel() == 0

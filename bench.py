@@ -8,14 +8,19 @@ hipGraph.  Prints ONE JSON line on stdout; progress goes to stderr.
 
 Timed regions (all on the stream the library launches on):
   1. K graph replays between two HIP events -> ms_per_step, value.
-  2. K eager forwards with a HIP event between consecutive C-ABI calls ->
+  2. K eager forwards queued back to back, a HIP event between consecutive
+     C-ABI calls ->
      average duration of each call's kernels (route+capacity+align, FC1,
      FC2, combine) -> TFLOP/s, GB/s and the roofline of the dominant kernel
      (FC1): HBM-bound at this shape (arithmetic intensity below the ridge).
   3. cpu_baseline: the CPU oracle on the same inputs (median of a few full
      forwards), rank 0 only.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant capacity|dropless]
+
+--variant dropless measures the dropless form instead (every route kept,
+block-padded segments, the extent a device scalar): its own JSON line, with
+the algorithmic work taken at the real padded extent.
 """
 
 from __future__ import annotations
@@ -62,6 +67,22 @@ def algorithmic_bytes(w, C, Cp, kept):
     }
 
 
+def algorithmic_bytes_dropless(w, X, Rd, BM):
+    """The same for the dropless form, whose FFN rows are the real padded
+    extent X (every route kept); Rd is the static bound of the route list."""
+    N, H, I, E, K = w.N, w.H, w.I, w.E, w.K
+    return {
+        # logits in; top-K ids/probs out and back in; per-route rank and
+        # per-expert counts; the route list to the extent, the block tags,
+        # block starts, the inverse, the per-token counts and the extent out
+        "route_dropless": N * E * 4 + N * K * (4 + 4) * 2 + N * K * 4 * 2 + E * 4 * 2
+                          + X * 8 + (Rd // BM) * 4 + E * 4 + N * K * 4 + N * 4 + 4,
+        "fc1": E * 2 * I * H * 2 + N * H * 2 + X * 8 + X * I * 2,
+        "fc2": E * H * I * 2 + X * I * 2 + X * H * 2,
+        "combine": N * K * H * 2 + N * K * 4 + N * H * 2,
+    }
+
+
 def roofline_fc1(flops, nbytes, us, traffic):
     """Roofline of the dominant kernel (FC1).  Its bound is whichever resource
     needs the longer time at peak: at C=256 the weight stream (HBM) outlasts
@@ -105,7 +126,7 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
-def cpu_baseline(T, w, forwards, min_seconds=12.0):
+def cpu_baseline(T, w, forwards, min_seconds=12.0, dropless=False):
     import numpy as np
     import moe_inputs
     import oracle
@@ -122,12 +143,15 @@ def cpu_baseline(T, w, forwards, min_seconds=12.0):
     times = []
     while len(times) < forwards or (sum(times) < min_seconds and len(times) < 20):
         t0 = time.perf_counter()
-        oracle.forward(lg, x, w1, w2, w.K, w.F)
+        if dropless:
+            oracle.dropless_forward(lg, x, w1, w2, w.K)
+        else:
+            oracle.forward(lg, x, w1, w2, w.K, w.F)
         times.append(time.perf_counter() - t0)
         log(f"  oracle forward {len(times)}: {times[-1]:.2f} s")
     med = statistics.median(times)
     return {"value": w.N / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(times)} full forwards of the {w.name} workload "
+            "sample": f"{len(times)} full {'dropless ' if dropless else ''}forwards of the {w.name} workload "
                       f"({sum(times):.1f} s in all, median {med:.2f} s), numpy float64 with {blas} BLAS"}
 
 
@@ -140,13 +164,15 @@ def main():
     ap.add_argument("--cpu-forwards", type=int, default=3,
                     help="minimum oracle forwards timed for cpu_baseline (more, up to 20, until 12 s of work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--variant", choices=["capacity", "dropless"], default="capacity",
+                    help="fixed-capacity forward (the headline) or the dropless form")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures the single-GPU MoE FFN forward only; runs on more than one GPU "
-              "are not part of this build (see DESIGN.md, 'Sharding')", file=sys.stderr)
+        print("bench.py measures the MoE FFN forward on one GPU only: it has no multi-GPU path, "
+              "since one GPU holds the whole layer's weights and tokens", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -162,12 +188,20 @@ def main():
         raise SystemExit("skewed workloads are parity cases, not bench lines")
     log(f"[bench] {w.name}: N={w.N} H={w.H} E={w.E} K={w.K} F={w.F} I={w.I}")
     T = moe_inputs.make_tensors(w, "cuda")
-    buf = moe.MoEBuffers(w.N, w.H, w.I, w.E, w.K, w.F, "cuda")
+    dropless = args.variant == "dropless"
+    if dropless:
+        buf = moe.DroplessBuffers(w.N, w.H, w.I, w.E, w.K, "cuda")
+        route = lambda: buf.route(T["logits"])                     # noqa: E731
+        route_name = "route_dropless"
+    else:
+        buf = moe.MoEBuffers(w.N, w.H, w.I, w.E, w.K, w.F, "cuda")
+        route = lambda: buf.route_capacity_align(T["logits"])      # noqa: E731
+        route_name = "route_capacity_align"
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
 
     def fwd():
-        buf.route_capacity_align(T["logits"])
+        route()
         buf.fc1_swiglu(T["x"], T["w1"])
         buf.fc2(T["w2"])
         buf.combine()
@@ -198,33 +232,45 @@ def main():
     log(f"[bench] graph replay: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
 
     # ---- timed region 2: eager, one HIP event between consecutive calls
-    names = ["route_capacity_align", "fc1", "fc2", "combine"]
-    calls = [lambda: buf.route_capacity_align(T["logits"]),
-             lambda: buf.fc1_swiglu(T["x"], T["w1"]), lambda: buf.fc2(T["w2"]), buf.combine]
+    names = [route_name, "fc1", "fc2", "combine"]
+    calls = [route, lambda: buf.fc1_swiglu(T["x"], T["w1"]), lambda: buf.fc2(T["w2"]), buf.combine]
+    # The steps are queued back to back with no host wait between them, so the
+    # host runs ahead and each interval holds the call's kernels, not the
+    # host's launch latency.
     tot = {n: 0.0 for n in names}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(args.steps)]
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             fwd()
         stream.synchronize()
-        for _ in range(args.steps):
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-            evs[0].record(stream)
+        for s in range(args.steps):
+            evs[s][0].record(stream)
             for i, c in enumerate(calls):
                 c()
-                evs[i + 1].record(stream)
-            stream.synchronize()
-            for i, n in enumerate(names):
-                tot[n] += evs[i].elapsed_time(evs[i + 1])
+                evs[s][i + 1].record(stream)
+        stream.synchronize()
+    for s in range(args.steps):
+        for i, n in enumerate(names):
+            tot[n] += evs[s][i].elapsed_time(evs[s][i + 1])
     us = {n: tot[n] / args.steps * 1e3 for n in names}
     log("[bench] eager per-call us: " + ", ".join(f"{n} {us[n]:.1f}" for n in names))
 
     kept = int((buf.token_routes >= 0).sum().item())
-    nbytes = algorithmic_bytes(w, buf.C, buf.Cp, kept)
-    fc1_flops = 2.0 * w.E * buf.Cp * (2 * w.I) * w.H
-    fc2_flops = 2.0 * w.E * buf.Cp * w.H * w.I
+    if dropless:
+        rows = int(buf.num_tokens_post_padded.item())
+        nbytes = algorithmic_bytes_dropless(w, rows, buf.R, buf.BM)
+        traffic = None      # the committed counters were taken on the capacity form
+        shape = {"R_bound": buf.R, "extent": rows, "timed": "hipGraph replay of the whole dropless forward"}
+    else:
+        rows = w.E * buf.Cp
+        nbytes = algorithmic_bytes(w, buf.C, buf.Cp, kept)
+        traffic = pmc_traffic(nbytes["fc1"])
+        shape = {"C": buf.C, "Cp": buf.Cp, "timed": "hipGraph replay of the whole forward"}
+    fc1_flops = 2.0 * rows * (2 * w.I) * w.H
+    fc2_flops = 2.0 * rows * w.H * w.I
     gemm_tflops = (fc1_flops + fc2_flops) / ((us["fc1"] + us["fc2"]) * 1e-6) / 1e12
     gbs = {n: nbytes[n] / (us[n] * 1e-6) / 1e9 for n in names}
-    traffic = pmc_traffic(nbytes["fc1"])
 
     rec = {
         "metric": METRIC,
@@ -239,8 +285,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.name, "N": w.N, "H": w.H, "E": w.E, "K": w.K, "F": w.F, "I": w.I,
-                   "C": buf.C, "Cp": buf.Cp, "timed": "hipGraph replay of the whole forward"},
+        "config": {"workload": w.name + ("/dropless" if dropless else ""), "N": w.N, "H": w.H,
+                   "E": w.E, "K": w.K, "I": w.I, **({} if dropless else {"F": w.F}), **shape},
         "routes_per_s": w.N * w.K / (ms_per_step * 1e-3),
         "gemm_tflops": gemm_tflops,
         "gemm_frac_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
@@ -252,7 +298,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the oracle")
-        rec["cpu_baseline"] = cpu_baseline(T, w, args.cpu_forwards)
+        rec["cpu_baseline"] = cpu_baseline(T, w, args.cpu_forwards, dropless=dropless)
     else:
         rec["cpu_baseline"] = None
     print(json.dumps(rec))

@@ -188,6 +188,19 @@ int moe_grouped_ffn_fwd_dropless(const uint16_t* x, const uint16_t* w1, const ui
                                  int64_t N, int32_t H, int32_t I, int32_t E, int32_t K,
                                  uint16_t* act, uint16_t* route_out, hipStream_t stream);
 
+/* moe_grouped_ffn_fwd_dropless as its two GEMM launches (for callers that
+ * schedule or time them separately); same arguments, same results. */
+int moe_grouped_fc1_swiglu_dropless(const uint16_t* x, const uint16_t* w1,
+                                    const int32_t* sorted_slot_ids, const float* slot_probs,
+                                    const int32_t* block_start,
+                                    const int32_t* num_tokens_post_padded, int64_t N, int32_t H,
+                                    int32_t I, int32_t E, int32_t K, uint16_t* act,
+                                    hipStream_t stream);
+int moe_grouped_fc2_dropless(const uint16_t* act, const uint16_t* w2, const int32_t* block_start,
+                             const int32_t* num_tokens_post_padded, int64_t N, int32_t H,
+                             int32_t I, int32_t E, int32_t K, uint16_t* route_out,
+                             hipStream_t stream);
+
 /* Step 4: permute-free grouped FFN ([PF] sections 2-3 and 6).
  *
  *   x          in  bf16 [N, H]      token-order activations, never permuted

@@ -15,7 +15,9 @@ from ._native import (  # noqa: F401
     moe_dropless_bound,
     moe_gather_combine,
     moe_grouped_fc1_swiglu,
+    moe_grouped_fc1_swiglu_dropless,
     moe_grouped_fc2,
+    moe_grouped_fc2_dropless,
     moe_grouped_ffn_fwd,
     moe_grouped_ffn_fwd_dropless,
     moe_layout_block_m,

@@ -38,6 +38,10 @@ _SIGNATURES = {
     "moe_route_dropless": (ctypes.c_int, [_vp, _i64, _i32, _i32] + [_vp] * 12),
     "moe_grouped_ffn_fwd_dropless": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32,
                                                                 _vp, _vp, _vp]),
+    "moe_grouped_fc1_swiglu_dropless": (ctypes.c_int, [_vp] * 6 + [_i64, _i32, _i32, _i32, _i32,
+                                                                   _vp, _vp]),
+    "moe_grouped_fc2_dropless": (ctypes.c_int, [_vp] * 4 + [_i64, _i32, _i32, _i32, _i32,
+                                                            _vp, _vp]),
     "moe_route_capacity": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp]),
     "moe_route_capacity_align": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
                                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
@@ -258,3 +262,29 @@ def moe_grouped_ffn_fwd_dropless(x, w1, w2, sorted_slot_ids, slot_probs, block_s
         _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"),
         N, H, I, E, K, _ptr(act, torch.bfloat16, R * I, "act"),
         _ptr(route_out, torch.bfloat16, R * H, "route_out"), _stream(stream)))
+
+
+def moe_grouped_fc1_swiglu_dropless(x, w1, sorted_slot_ids, slot_probs, block_start,
+                                    num_tokens_post_padded, K: int, act, stream=None):
+    N, H = x.shape
+    E, I2, _ = w1.shape
+    I = I2 // 2
+    R = moe_dropless_bound(N, K, E)
+    _check("moe_grouped_fc1_swiglu_dropless", lib.moe_grouped_fc1_swiglu_dropless(
+        _ptr(x, torch.bfloat16, N * H, "x"), _ptr(w1, torch.bfloat16, E * 2 * I * H, "w1"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"),
+        _ptr(slot_probs, torch.float32, R, "slot_probs"),
+        _ptr(block_start, torch.int32, E, "block_start"),
+        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"),
+        N, H, I, E, K, _ptr(act, torch.bfloat16, R * I, "act"), _stream(stream)))
+
+
+def moe_grouped_fc2_dropless(act, w2, block_start, num_tokens_post_padded, N: int, K: int,
+                             route_out, stream=None):
+    E, H, I = w2.shape
+    R = moe_dropless_bound(N, K, E)
+    _check("moe_grouped_fc2_dropless", lib.moe_grouped_fc2_dropless(
+        _ptr(act, torch.bfloat16, R * I, "act"), _ptr(w2, torch.bfloat16, E * H * I, "w2"),
+        _ptr(block_start, torch.int32, E, "block_start"),
+        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"),
+        N, H, I, E, K, _ptr(route_out, torch.bfloat16, R * H, "route_out"), _stream(stream)))

@@ -27,6 +27,7 @@
 //     N-tiles, sharing the gathered A rows) land on the same XCD and its L2.
 #include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <initializer_list>
 
 #include "moe_common.h"
@@ -195,6 +196,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
                   "whole DMA blocks per wave");
     static_assert(NA >= 2 && NB >= 2 && WAIT + STORES < 64, "stage rings");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(!DYN || LDS_BYTES >= (3 * kMaxE + 1) * 4, "room for the tile list");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
 
@@ -238,38 +240,52 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         d.seg = d.e * p.Cp;
         d.len = p.Cp;
     };
-    // Variable segments: a cursor walks the experts (tile indices only grow
-    // within a workgroup), reading the block starts through the scalar cache.
+    // ---- variable segments.  Tiles are numbered expert by expert and, within
+    // an expert, column tile by column tile with the row tiles innermost, so
+    // the row tiles of one weight panel run side by side (consecutive tiles
+    // share an XCD) and read it from L2 together.  The block starts are device
+    // data: segments are clamped to the route list, never trusted.
     typedef const __attribute__((address_space(4))) int* const_int_ptr;
     const const_int_ptr bs = (const_int_ptr)(p.block_start);
-    // Device data is range-checked, never trusted: segments are clamped to
-    // the route list.
-    int cur_e = 0, mt_before = 0, cur_start = 0, cur_len = 0;
     int extent_slots = 0;
-    auto segment = [&](int e) {
-        const int lo = min(max(bs[e], 0), p.R / kBlockM) * kBlockM;
-        const int hi = e + 1 < p.E ? min(max(bs[e + 1], 0), p.R / kBlockM) * kBlockM : extent_slots;
-        cur_start = lo;
-        cur_len = max(hi - lo, 0);
+    auto seg_lo = [&](int v) { return min(max(v, 0), p.R / kBlockM) * kBlockM; };
+    auto tiles_of = [&](int len) { return (len + BMT - 1) / BMT * p.NT; };
+    auto set_tile = [&](Tile& d, int e, int nt, int mi, int seg, int len) {
+        d.e = e;
+        d.nt = nt;
+        d.m0 = mi * BMT;
+        d.rot = (e * kKRotate) % KT;
+        d.seg = seg;
+        d.len = len;
     };
-    if (DYN) {
-        extent_slots = min(max(((const_int_ptr)(p.extent))[0], 0), p.R);
-        segment(0);
-    }
-    auto find = [&](int t, Tile& d) -> bool {   // DYN: tile t, or false past the last
-        const int mtile = t / p.NT;
-        while (cur_e < p.E && mtile >= mt_before + (cur_len + BMT - 1) / BMT) {
-            mt_before += (cur_len + BMT - 1) / BMT;
+    // Lane k of every wave holds the workgroup's k-th tile (t0 + k*G), built
+    // once before the loads start: expert (-1 past the last tile), column
+    // tile | row tile << 16, segment start, segment length.
+    int lt_e = -1, lt_ntm = 0, lt_seg = 0, lt_len = 0;
+    // Past 64 tiles a cursor walks the experts in the same numbering,
+    // reading the block starts through the scalar cache.
+    int cur_e = -1, t_before = 0, cur_start = 0, cur_len = 0;
+    auto find = [&](int k, int t, Tile& d) -> bool {   // the k-th tile t, or false past the last
+        if (k < kWave) {
+            const int e = __builtin_amdgcn_readlane(lt_e, k);
+            if (e < 0) return false;
+            const int ntm = __builtin_amdgcn_readlane(lt_ntm, k);
+            set_tile(d, e, ntm & 0xffff, ntm >> 16, __builtin_amdgcn_readlane(lt_seg, k),
+                     __builtin_amdgcn_readlane(lt_len, k));
+            return true;
+        }
+        while (cur_e < p.E && (cur_e < 0 || t >= t_before + tiles_of(cur_len))) {
+            if (cur_e >= 0) t_before += tiles_of(cur_len);
             ++cur_e;
-            if (cur_e < p.E) segment(cur_e);
+            if (cur_e < p.E) {
+                cur_start = seg_lo(bs[cur_e]);
+                const int hi = cur_e + 1 < p.E ? seg_lo(bs[cur_e + 1]) : extent_slots;
+                cur_len = max(hi - cur_start, 0);
+            }
         }
         if (cur_e >= p.E) return false;
-        d.nt = t % p.NT;
-        d.e = cur_e;
-        d.m0 = (mtile - mt_before) * BMT;
-        d.rot = (d.e * kKRotate) % KT;
-        d.seg = cur_start;
-        d.len = cur_len;
+        const int r = t - t_before, mt = (cur_len + BMT - 1) / BMT;
+        set_tile(d, cur_e, r / mt, r % mt, cur_start, cur_len);
         return true;
     };
     auto kslab = [&](const Tile& d, int kt) {   // the K slab a tile fetches at its step kt
@@ -379,9 +395,58 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
 
     // ---- the block's first tile and the prologue (the steps before step 0)
     int t = xcd_remap(blockIdx.x, G);   // fixed segments: < tiles (the host caps G)
-    Tile cur, nxt;
     if (DYN) {
-        if (!find(t, cur)) return;       // more workgroups than tiles: nothing to do
+        // The tile list, built in LDS before any load lands there: per expert
+        // its segment and the tiles before it (a scan), then per lane k a
+        // binary search for tile t + k*G.
+        int* s_tp = reinterpret_cast<int*>(smem);            // [E + 1] tiles before expert e
+        int* s_lo = s_tp + kMaxE + 1;                         // [E] segment start
+        int* s_len = s_lo + kMaxE;                            // [E] segment length
+        extent_slots = min(max(((const_int_ptr)(p.extent))[0], 0), p.R);
+        for (int e = threadIdx.x; e < p.E; e += NW * kWave) {
+            const int lo = seg_lo(p.block_start[e]);
+            const int hi = e + 1 < p.E ? seg_lo(p.block_start[e + 1]) : extent_slots;
+            const int len = max(hi - lo, 0);
+            s_lo[e] = lo;
+            s_len[e] = len;
+            s_tp[e + 1] = tiles_of(len);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            int carry = 0;
+            for (int b = 0; b < p.E; b += kWave) {
+                const int e = b + lane;
+                int v = e < p.E ? s_tp[e + 1] : 0;
+#pragma unroll
+                for (int d = 1; d < kWave; d <<= 1) {
+                    const int u = __shfl_up(v, d);
+                    if (lane >= d) v += u;
+                }
+                if (e < p.E) s_tp[e + 1] = v + carry;
+                carry += __shfl(v, kWave - 1);
+            }
+            if (lane == 0) s_tp[0] = 0;
+        }
+        __syncthreads();
+        const int tk = t + lane * G;
+        if (tk < s_tp[p.E]) {
+            int lo = 0, hi = p.E;                             // s_tp[lo] <= tk < s_tp[hi]
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (s_tp[mid] <= tk) lo = mid; else hi = mid;
+            }
+            const int r = tk - s_tp[lo], mt = (s_len[lo] + BMT - 1) / BMT;
+            lt_e = lo;
+            lt_ntm = (r / mt) | ((r % mt) << 16);
+            lt_seg = s_lo[lo];
+            lt_len = s_len[lo];
+        }
+        __syncthreads();   // the list is read: the LDS belongs to the load rings from here on
+    }
+    Tile cur, nxt;
+    int k = 0;                           // cur is the workgroup's k-th tile
+    if (DYN) {
+        if (!find(0, t, cur)) return;    // more workgroups than tiles: nothing to do
     } else {
         decode(t, cur);
     }
@@ -447,7 +512,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         const int tn = t + G;
         bool has_next;
         if (DYN) {
-            has_next = find(tn, nxt);
+            has_next = find(k + 1, tn, nxt);
         } else {
             has_next = tn < p.tiles;
             if (has_next) decode(tn, nxt);
@@ -551,6 +616,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         first = false;
         if (!has_next) break;
         t = tn;
+        ++k;
         cur.e = nxt.e;
         cur.m0 = nxt.m0;
         cur.nt = nxt.nt;
@@ -627,15 +693,28 @@ int pick_tile_m(int Cp) {
     return best;
 }
 
-// rows: slots per expert (fixed segments: Cp; variable: the expected
-// padded load, which only steers the tile shape)
-int launch(const FfnArgs& a, bool fc1, int E, hipStream_t s, bool dyn = false, int rows = 0) {
+// Variable segments: every row tile of an expert streams its weight panel
+// (from HBM or, beside a sibling tile, from L2), so the tile should hold a
+// typical segment whole.  With routes spread evenly a segment holds about
+// mean +- sqrt(mean) slots; the tile covers mean + 2 sqrt(mean), up to the
+// largest shape.
+int pick_tile_dyn(double mean) {
+    const double est = mean + 2.0 * std::sqrt(mean);
+    if (est > 128.0) return 256;
+    if (est > 64.0) return 128;
+    if (est > 32.0) return 64;
+    return 32;
+}
+
+// Fixed segments tile Cp; variable ones (dyn) take their shape from the mean
+// number of routes per expert, which only steers performance.
+int launch(const FfnArgs& a, bool fc1, int E, hipStream_t s, bool dyn = false, double mean = 0.0) {
     if (a.Kdim < 128) {
         // a 64-long contraction: 32-wide K slabs, so a tile has the two
         // steps the cross-tile look-ahead needs
         return launch_gemm<32, 128, 1, 2, 32, 2, 3>(a, fc1, E, s, dyn);
     }
-    switch (pick_tile_m(dyn ? rows : a.Cp)) {
+    switch (dyn ? pick_tile_dyn(mean) : pick_tile_m(a.Cp)) {
         // 64-wide K slabs (128 contiguous bytes per weight row per step keep the
         // HBM stream efficient); rings sized to the 160 KB LDS.
         case 256: return launch_gemm<256, 256, 2, 4, 64, 2, 3>(a, fc1, E, s, dyn);
@@ -736,13 +815,16 @@ extern "C" int moe_grouped_ffn_fwd(const uint16_t* x, const uint16_t* w1, const 
     return st != MOE_OK ? st : launch_status();
 }
 
-extern "C" int moe_grouped_ffn_fwd_dropless(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
-                                            const int32_t* sorted_slot_ids, const float* slot_probs,
-                                            const int32_t* block_start,
-                                            const int32_t* num_tokens_post_padded, int64_t N,
-                                            int32_t H, int32_t I, int32_t E, int32_t K,
-                                            uint16_t* act, uint16_t* route_out, hipStream_t stream) {
-    using namespace moe;
+namespace moe {
+namespace {
+
+// Host checks and arguments of the dropless FFN calls; which = 1 (FC1),
+// 2 (FC2) or 3 (both).
+int ffn_dropless(int which, const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                 const int32_t* sorted_slot_ids, const float* slot_probs,
+                 const int32_t* block_start, const int32_t* num_tokens_post_padded, int64_t N,
+                 int32_t H, int32_t I, int32_t E, int32_t K, uint16_t* act, uint16_t* route_out,
+                 hipStream_t stream) {
     if (N < 0 || E < 1 || K < 1 || K > E) return MOE_ERR_INVALID_ARG;
     int st = check_dims(H, I);
     if (st != MOE_OK) return st;
@@ -754,21 +836,64 @@ extern "C" int moe_grouped_ffn_fwd_dropless(const uint16_t* x, const uint16_t* w
         static_cast<int64_t>(2) * I * H * 2 >= big)
         return MOE_ERR_UNSUPPORTED;
     if (N == 0) return MOE_OK;
-    st = check_ptrs({x, w1, w2, sorted_slot_ids, slot_probs, block_start, num_tokens_post_padded,
-                     act, route_out});
-    if (st != MOE_OK) return st;
-    // the tile shape follows the mean padded load per expert
-    const int rows = static_cast<int>((N * K / E + kBlockM - 1) / kBlockM * kBlockM);
-    FfnArgs a1 = fc1_args(x, w1, sorted_slot_ids, slot_probs, N, H, I, 0, act);
-    a1.block_start = block_start;
-    a1.extent = num_tokens_post_padded;
-    a1.R = static_cast<int>(R);
-    st = launch(a1, true, E, stream, true, std::max(rows, kBlockM));
-    if (st != MOE_OK) return st;
-    FfnArgs a2 = fc2_args(act, w2, N, H, I, 0, route_out);
-    a2.block_start = block_start;
-    a2.extent = num_tokens_post_padded;
-    a2.R = static_cast<int>(R);
-    st = launch(a2, false, E, stream, true, std::max(rows, kBlockM));
-    return st != MOE_OK ? st : launch_status();
+    if (which & 1) {
+        st = check_ptrs({x, w1, sorted_slot_ids, slot_probs, block_start, num_tokens_post_padded, act});
+        if (st != MOE_OK) return st;
+    }
+    if (which & 2) {
+        st = check_ptrs({act, w2, block_start, num_tokens_post_padded, route_out});
+        if (st != MOE_OK) return st;
+    }
+    // the tile shape follows the mean load per expert
+    const double mean = static_cast<double>(N) * K / E;
+    if (which & 1) {
+        FfnArgs a1 = fc1_args(x, w1, sorted_slot_ids, slot_probs, N, H, I, 0, act);
+        a1.block_start = block_start;
+        a1.extent = num_tokens_post_padded;
+        a1.R = static_cast<int>(R);
+        st = launch(a1, true, E, stream, true, mean);
+        if (st != MOE_OK) return st;
+    }
+    if (which & 2) {
+        FfnArgs a2 = fc2_args(act, w2, N, H, I, 0, route_out);
+        a2.block_start = block_start;
+        a2.extent = num_tokens_post_padded;
+        a2.R = static_cast<int>(R);
+        st = launch(a2, false, E, stream, true, mean);
+        if (st != MOE_OK) return st;
+    }
+    return launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_grouped_ffn_fwd_dropless(const uint16_t* x, const uint16_t* w1, const uint16_t* w2,
+                                            const int32_t* sorted_slot_ids, const float* slot_probs,
+                                            const int32_t* block_start,
+                                            const int32_t* num_tokens_post_padded, int64_t N,
+                                            int32_t H, int32_t I, int32_t E, int32_t K,
+                                            uint16_t* act, uint16_t* route_out, hipStream_t stream) {
+    return moe::ffn_dropless(3, x, w1, w2, sorted_slot_ids, slot_probs, block_start,
+                             num_tokens_post_padded, N, H, I, E, K, act, route_out, stream);
+}
+
+extern "C" int moe_grouped_fc1_swiglu_dropless(const uint16_t* x, const uint16_t* w1,
+                                               const int32_t* sorted_slot_ids,
+                                               const float* slot_probs, const int32_t* block_start,
+                                               const int32_t* num_tokens_post_padded, int64_t N,
+                                               int32_t H, int32_t I, int32_t E, int32_t K,
+                                               uint16_t* act, hipStream_t stream) {
+    return moe::ffn_dropless(1, x, w1, nullptr, sorted_slot_ids, slot_probs, block_start,
+                             num_tokens_post_padded, N, H, I, E, K, act, nullptr, stream);
+}
+
+extern "C" int moe_grouped_fc2_dropless(const uint16_t* act, const uint16_t* w2,
+                                        const int32_t* block_start,
+                                        const int32_t* num_tokens_post_padded, int64_t N,
+                                        int32_t H, int32_t I, int32_t E, int32_t K,
+                                        uint16_t* route_out, hipStream_t stream) {
+    return moe::ffn_dropless(2, nullptr, nullptr, w2, nullptr, nullptr, block_start,
+                             num_tokens_post_padded, N, H, I, E, K, const_cast<uint16_t*>(act),
+                             route_out, stream);
 }

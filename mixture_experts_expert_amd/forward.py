@@ -126,6 +126,15 @@ class DroplessBuffers:
                                          self.block_start, self.num_tokens_post_padded, self.K,
                                          self.act, self.route_out, stream)
 
+    def fc1_swiglu(self, x, w1, stream=None):
+        nat.moe_grouped_fc1_swiglu_dropless(x, w1, self.sorted_slot_ids, self.slot_probs,
+                                            self.block_start, self.num_tokens_post_padded,
+                                            self.K, self.act, stream)
+
+    def fc2(self, w2, stream=None):
+        nat.moe_grouped_fc2_dropless(self.act, w2, self.block_start, self.num_tokens_post_padded,
+                                     self.N, self.K, self.route_out, stream)
+
     def combine(self, stream=None):
         nat.moe_gather_combine(self.route_out, self.token_routes, self.y, stream)
 

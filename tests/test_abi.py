@@ -20,7 +20,8 @@ def test_every_declared_symbol_is_exported():
     assert set(names) == {"moe_status_string", "moe_source_capacity", "moe_layout_block_m",
                           "moe_padded_capacity", "moe_route_capacity", "moe_route_capacity_align",
                           "moe_align", "moe_dropless_bound", "moe_route_dropless",
-                          "moe_grouped_ffn_fwd_dropless",
+                          "moe_grouped_ffn_fwd_dropless", "moe_grouped_fc1_swiglu_dropless",
+                          "moe_grouped_fc2_dropless",
                           "moe_grouped_ffn_fwd", "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
                           "moe_gather_combine"}
     for n in names:

@@ -144,3 +144,20 @@ def test_dropless_n_zero_is_noop():
          "w2": torch.zeros(4, 64, 64, dtype=torch.bfloat16, device=DEV)}
     run(buf, T)
     assert buf.y.numel() == 0
+
+
+def test_dropless_split_equals_fused_call():
+    w = moe_inputs.WORKLOADS["small_qwen3moe_n1024_h512_e8_k2"]
+    T = moe_inputs.make_tensors(w, DEV)
+    a = DroplessBuffers(w.N, w.H, w.I, w.E, w.K, DEV)
+    run(a, T)
+    b = DroplessBuffers(w.N, w.H, w.I, w.E, w.K, DEV)
+    b.route(T["logits"])
+    b.fc1_swiglu(T["x"], T["w1"])
+    b.fc2(T["w2"])
+    b.combine()
+    torch.cuda.synchronize()
+    ext = int(a.num_tokens_post_padded.item())
+    for k in ("act", "route_out"):
+        assert torch.equal(getattr(a, k)[:ext], getattr(b, k)[:ext]), k
+    assert torch.equal(a.y, b.y)

@@ -126,6 +126,19 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
+def warm(fn, steps, seconds, stream):
+    """Untimed warm-up: at least `steps` calls and at least `seconds` of
+    back-to-back work, so clocks and power state settle before timing (a few
+    milliseconds of work leaves the first timed steps ~10% slow)."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < steps or time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        n += 10
+        stream.synchronize()
+
+
 def cpu_baseline(T, w, forwards, min_seconds=12.0, dropless=False):
     import numpy as np
     import moe_inputs
@@ -160,6 +173,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup-seconds", type=float, default=0.5,
+                    help="minimum wall time of untimed warm-up before each timed region")
     ap.add_argument("--workload", default=None, help="workload name (default: the Qwen3-30B-A3B-shaped layer)")
     ap.add_argument("--cpu-forwards", type=int, default=3,
                     help="minimum oracle forwards timed for cpu_baseline (more, up to 20, until 12 s of work)")
@@ -217,9 +232,7 @@ def main():
 
     # ---- timed region 1: graph replays
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            graph.replay()
-        stream.synchronize()
+        warm(graph.replay, args.warmup, args.warmup_seconds, stream)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         ev0.record(stream)
@@ -241,9 +254,7 @@ def main():
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
            for _ in range(args.steps)]
     with torch.cuda.stream(stream):
-        for _ in range(args.warmup):
-            fwd()
-        stream.synchronize()
+        warm(fwd, args.warmup, args.warmup_seconds, stream)
         for s in range(args.steps):
             evs[s][0].record(stream)
             for i, c in enumerate(calls):

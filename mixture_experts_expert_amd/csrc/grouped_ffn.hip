@@ -683,8 +683,11 @@ int launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s, bool dyn = false) {
 }
 
 // M-tile: the one (of 256, 128, 64, 32) that pads Cp the least; ties go to
-// the larger tile (fewer re-reads of each weight panel).
+// the larger tile (fewer re-reads of each weight panel).  A 320-slot segment
+// is the exception.
 int pick_tile_m(int Cp) {
+    // a segment of exactly 320 slots takes one 320-row tile: one weight pass
+    if (Cp == 320) return 320;
     int best = 256, best_rows = (Cp + 255) / 256 * 256;
     for (int t : {128, 64, 32}) {
         const int rows = (Cp + t - 1) / t * t;
@@ -696,10 +699,14 @@ int pick_tile_m(int Cp) {
 // Variable segments: every row tile of an expert streams its weight panel
 // (from HBM or, beside a sibling tile, from L2), so the tile should hold a
 // typical segment whole.  With routes spread evenly a segment holds about
-// mean +- sqrt(mean) slots; the tile covers mean + 2 sqrt(mean), up to the
-// largest shape.
+// mean +- sqrt(mean) slots; the tile covers mean + 2 sqrt(mean).  Just past
+// 256 rows a 320-row tile keeps one weight pass per expert (its LDS leaves
+// room for two weight stages only, which costs less than a second, mostly
+// empty row tile that streams the panel again); well past it the segments
+// take several 256-row tiles either way.
 int pick_tile_dyn(double mean) {
     const double est = mean + 2.0 * std::sqrt(mean);
+    if (est > 256.0 && est <= 320.0) return 320;
     if (est > 128.0) return 256;
     if (est > 64.0) return 128;
     if (est > 32.0) return 64;
@@ -717,6 +724,7 @@ int launch(const FfnArgs& a, bool fc1, int E, hipStream_t s, bool dyn = false, d
     switch (dyn ? pick_tile_dyn(mean) : pick_tile_m(a.Cp)) {
         // 64-wide K slabs (128 contiguous bytes per weight row per step keep the
         // HBM stream efficient); rings sized to the 160 KB LDS.
+        case 320: return launch_gemm<320, 256, 2, 4, 64, 2, 2>(a, fc1, E, s, dyn);
         case 256: return launch_gemm<256, 256, 2, 4, 64, 2, 3>(a, fc1, E, s, dyn);
         case 128: return launch_gemm<128, 256, 2, 4, 64, 2, 3>(a, fc1, E, s, dyn);
         case 64: return launch_gemm<64, 128, 2, 2, 64, 2, 3>(a, fc1, E, s, dyn);

@@ -16,7 +16,8 @@ Pages followed (cited by title and section):
   the sync-free align, gather-in-GEMM FC1 -> SwiGLU -> FC2 and the
   gather-combine.
 
-Parity status per function is listed in ``oracle.moe``'s module docstring.
+Parity status per function is listed in the module docstrings of
+``oracle.moe`` (forward) and ``oracle.backward`` (backward).
 """
 
 from .moe import (  # noqa: F401
@@ -39,4 +40,12 @@ from .moe import (  # noqa: F401
     permuted_forward,
     route_topk,
     source_capacity,
+)
+from .backward import (  # noqa: F401
+    backward,
+    expert_backward,
+    fc1_preact,
+    grouped_ffn_backward,
+    route_backward,
+    swiglu_backward,
 )

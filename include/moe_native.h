@@ -244,6 +244,93 @@ int moe_grouped_fc2(const uint16_t* act, const uint16_t* w2, int64_t N, int32_t 
 int moe_gather_combine(const uint16_t* route_out, const int32_t* token_routes, int64_t N,
                        int32_t K, int32_t H, int64_t R, uint16_t* y, hipStream_t stream);
 
+/* ------------------------------------------------------------------------
+ * Backward (training) of the fixed-capacity layer
+ *
+ * [PF] sections 3, 5 and 6: the forward keeps only the 2I pre-activation;
+ * the backward gathers dy through the same route list (FC2 dgrad), recomputes
+ * the gated activation and differentiates it together with the route
+ * probability, contracts against the transposed weights (FC1 dgrad), reduces
+ * the per-route input gradients to token rows with moe_gather_combine, and
+ * forms the weight gradients by contracting over each expert's slots (one
+ * owner per dW tile, no atomics).  Order, on one stream:
+ *
+ *   moe_grouped_fc1_swiglu_save   (forward FC1, also storing the pre-activation)
+ *   moe_grouped_fc2 + moe_gather_combine   (rest of the forward)
+ *   moe_grouped_fc2_dgrad   d_act  = dy[row(s)] @ W2[e]
+ *   moe_swiglu_bwd          act (recomputed), d_preact, d_prob
+ *   moe_grouped_fc1_dgrad   d_a    = d_preact[s] @ W1[e]
+ *   moe_gather_combine      dx[t]  = sum over t's kept routes of d_a
+ *   moe_grouped_fc2_wgrad   dW2[e] = sum_s dy[row(s)]^T act[s]
+ *   moe_grouped_fc1_wgrad   dW1[e] = sum_s d_preact[s]^T x[row(s)]
+ *   moe_route_bwd           d_logits through the top-K softmax
+ *
+ * row(s) = sorted_slot_ids[s]; pad slots (row N) contribute nothing.  All
+ * bf16 results are rounded once (nearest-even) from float32 accumulators.
+ * The sizes and envelope are the forward's (N, H, I, E, C as there, R = E*Cp);
+ * outputs are fully overwritten (dW included: no accumulation into them),
+ * except that N == 0 or C == 0 is a no-op that leaves every output as it was.
+ * ------------------------------------------------------------------------ */
+
+/* moe_grouped_fc1_swiglu that also stores the raw FC1 product
+ * h = x[row(s)] @ W1[e]^T as bf16:  preact  out bf16 [R, 2I], row s =
+ * [gate (I) | up (I)].  act is the same as moe_grouped_fc1_swiglu's. */
+int moe_grouped_fc1_swiglu_save(const uint16_t* x, const uint16_t* w1,
+                                const int32_t* sorted_slot_ids, const float* slot_probs,
+                                int64_t N, int32_t H, int32_t I, int32_t E, int64_t C,
+                                uint16_t* act, uint16_t* preact, hipStream_t stream);
+
+/* FC2 data gradient:  d_act[s] = bf16( dy[row(s)] @ W2[e] ), e = s / Cp.
+ *   dy      in  bf16 [N, H]  gradient of y, token order (never permuted)
+ *   w2      in  bf16 [E, H, I]
+ *   d_act   out bf16 [R, I]  (pad slots: zeros) */
+int moe_grouped_fc2_dgrad(const uint16_t* dy, const uint16_t* w2, const int32_t* sorted_slot_ids,
+                          int64_t N, int32_t H, int32_t I, int32_t E, int64_t C, uint16_t* d_act,
+                          hipStream_t stream);
+
+/* Gated-activation recompute + backward, one pass over R slot rows ([PF]
+ * section 6), with g = preact[s, :I], u = preact[s, I:], p = slot_probs[s],
+ * sig = sigmoid(g):
+ *   act[s]          = bf16( silu(g) * u * p )
+ *   d_preact[s, :I] = bf16( d_act * p * u * sig * (1 + g * (1 - sig)) )
+ *   d_preact[s, I:] = bf16( d_act * p * silu(g) )
+ *   d_prob[s]       = float32 sum over the row of d_act * silu(g) * u
+ *   preact in bf16 [R, 2I], d_act in bf16 [R, I], slot_probs in f32 [R];
+ *   act out bf16 [R, I], d_preact out bf16 [R, 2I], d_prob out f32 [R]. */
+int moe_swiglu_bwd(const uint16_t* preact, const uint16_t* d_act, const float* slot_probs,
+                   int64_t R, int32_t I, uint16_t* act, uint16_t* d_preact, float* d_prob,
+                   hipStream_t stream);
+
+/* FC1 data gradient, per route:  d_a[s] = bf16( d_preact[s] @ W1[e] ).
+ *   d_preact in bf16 [R, 2I], w1 in bf16 [E, 2I, H], d_a out bf16 [R, H].
+ * dx follows as moe_gather_combine(d_a, token_routes, ...). */
+int moe_grouped_fc1_dgrad(const uint16_t* d_preact, const uint16_t* w1, int64_t N, int32_t H,
+                          int32_t I, int32_t E, int64_t C, uint16_t* d_a, hipStream_t stream);
+
+/* FC2 weight gradient:  dW2[e] = bf16( sum over e's slots s of dy[row(s)]^T act[s] ).
+ *   dy in bf16 [N, H], act in bf16 [R, I] (moe_swiglu_bwd's recompute),
+ *   dw2 out bf16 [E, H, I]. */
+int moe_grouped_fc2_wgrad(const uint16_t* dy, const uint16_t* act, const int32_t* sorted_slot_ids,
+                          int64_t N, int32_t H, int32_t I, int32_t E, int64_t C, uint16_t* dw2,
+                          hipStream_t stream);
+
+/* FC1 weight gradient:  dW1[e] = bf16( sum over e's slots s of d_preact[s]^T x[row(s)] ).
+ *   d_preact in bf16 [R, 2I], x in bf16 [N, H], dw1 out bf16 [E, 2I, H]. */
+int moe_grouped_fc1_wgrad(const uint16_t* d_preact, const uint16_t* x,
+                          const int32_t* sorted_slot_ids, int64_t N, int32_t H, int32_t I,
+                          int32_t E, int64_t C, uint16_t* dw1, hipStream_t stream);
+
+/* Router-logit gradient through the softmax over each token's top K.  Route
+ * (t, k) takes dp = d_prob[token_routes[t, k]] (0 if dropped, or if the index
+ * is outside [0, R)); with p = topk_probs[t]:
+ *   d_logits[t, topk_ids[t, k]] = p_k * (dp_k - sum_j p_j dp_j), 0 elsewhere.
+ *   topk_ids in int32 [N, K], topk_probs in f32 [N, K], token_routes in
+ *   int32 [N, K], d_prob in f32 [R]; d_logits out f32 [N, E] (every entry
+ *   written). */
+int moe_route_bwd(const int32_t* topk_ids, const float* topk_probs, const int32_t* token_routes,
+                  const float* d_prob, int64_t N, int32_t E, int32_t K, int64_t R,
+                  float* d_logits, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

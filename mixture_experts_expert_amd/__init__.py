@@ -1,4 +1,4 @@
-"""MI355X-native capacity-padded, permute-free MoE FFN forward.
+"""MI355X-native capacity-padded, permute-free MoE FFN forward and backward.
 
 The compute lives in libmoe_native.so (hand-written HIP for gfx950, C ABI in
 include/moe_native.h); this package is its thin ctypes binding plus a
@@ -14,18 +14,31 @@ from ._native import (  # noqa: F401
     moe_align,
     moe_dropless_bound,
     moe_gather_combine,
+    moe_grouped_fc1_dgrad,
     moe_grouped_fc1_swiglu,
     moe_grouped_fc1_swiglu_dropless,
+    moe_grouped_fc1_swiglu_save,
+    moe_grouped_fc1_wgrad,
     moe_grouped_fc2,
+    moe_grouped_fc2_dgrad,
     moe_grouped_fc2_dropless,
+    moe_grouped_fc2_wgrad,
     moe_grouped_ffn_fwd,
     moe_grouped_ffn_fwd_dropless,
     moe_layout_block_m,
     moe_padded_capacity,
+    moe_route_bwd,
     moe_route_capacity,
     moe_route_capacity_align,
     moe_route_dropless,
     moe_source_capacity,
     moe_status_string,
+    moe_swiglu_bwd,
 )
-from .forward import DroplessBuffers, MoEBuffers, forward, forward_dropless  # noqa: F401
+from .forward import (  # noqa: F401
+    DroplessBuffers,
+    MoEBackwardBuffers,
+    MoEBuffers,
+    forward,
+    forward_dropless,
+)

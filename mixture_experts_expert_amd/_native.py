@@ -53,6 +53,17 @@ _SIGNATURES = {
                                               _vp, _vp]),
     "moe_grouped_fc2": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _vp]),
     "moe_gather_combine": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i64, _vp, _vp]),
+    "moe_grouped_fc1_swiglu_save": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                                   _i64, _vp, _vp, _vp]),
+    "moe_grouped_fc2_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp,
+                                             _vp]),
+    "moe_swiglu_bwd": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _vp, _vp, _vp, _vp]),
+    "moe_grouped_fc1_dgrad": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _vp]),
+    "moe_grouped_fc2_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp,
+                                             _vp]),
+    "moe_grouped_fc1_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp,
+                                             _vp]),
+    "moe_route_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i64, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -288,3 +299,95 @@ def moe_grouped_fc2_dropless(act, w2, block_start, num_tokens_post_padded, N: in
         _ptr(block_start, torch.int32, E, "block_start"),
         _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"),
         N, H, I, E, K, _ptr(route_out, torch.bfloat16, R * H, "route_out"), _stream(stream)))
+
+
+# ---------------------------------------------------------------- backward
+
+def _ffn_shape(x, w1):
+    N, H = x.shape
+    E, I2, H1 = w1.shape
+    if H1 != H or I2 % 2:
+        raise ValueError("w1 must be [E, 2I, H] with x [N, H]")
+    return N, H, I2 // 2, E
+
+
+def moe_grouped_fc1_swiglu_save(x, w1, sorted_slot_ids, slot_probs, C: int, act, preact,
+                                stream=None):
+    N, H, I, E = _ffn_shape(x, w1)
+    R = E * moe_padded_capacity(C)
+    _check("moe_grouped_fc1_swiglu_save", lib.moe_grouped_fc1_swiglu_save(
+        _ptr(x, torch.bfloat16, N * H, "x"), _ptr(w1, torch.bfloat16, E * 2 * I * H, "w1"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"),
+        _ptr(slot_probs, torch.float32, R, "slot_probs"), N, H, I, E, C,
+        _ptr(act, torch.bfloat16, R * I, "act"), _ptr(preact, torch.bfloat16, R * 2 * I, "preact"),
+        _stream(stream)))
+
+
+def moe_grouped_fc2_dgrad(dy, w2, sorted_slot_ids, C: int, d_act, stream=None):
+    N, H = dy.shape
+    E, H2, I = w2.shape
+    if H2 != H:
+        raise ValueError("w2 must be [E, H, I] with dy [N, H]")
+    R = E * moe_padded_capacity(C)
+    _check("moe_grouped_fc2_dgrad", lib.moe_grouped_fc2_dgrad(
+        _ptr(dy, torch.bfloat16, N * H, "dy"), _ptr(w2, torch.bfloat16, E * H * I, "w2"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"), N, H, I, E, C,
+        _ptr(d_act, torch.bfloat16, R * I, "d_act"), _stream(stream)))
+
+
+def moe_swiglu_bwd(preact, d_act, slot_probs, act, d_preact, d_prob, stream=None):
+    R, I = d_act.shape
+    _check("moe_swiglu_bwd", lib.moe_swiglu_bwd(
+        _ptr(preact, torch.bfloat16, R * 2 * I, "preact"),
+        _ptr(d_act, torch.bfloat16, R * I, "d_act"),
+        _ptr(slot_probs, torch.float32, R, "slot_probs"), R, I,
+        _ptr(act, torch.bfloat16, R * I, "act"),
+        _ptr(d_preact, torch.bfloat16, R * 2 * I, "d_preact"),
+        _ptr(d_prob, torch.float32, R, "d_prob"), _stream(stream)))
+
+
+def moe_grouped_fc1_dgrad(d_preact, w1, N: int, C: int, d_a, stream=None):
+    E, I2, H = w1.shape
+    I = I2 // 2
+    R = E * moe_padded_capacity(C)
+    _check("moe_grouped_fc1_dgrad", lib.moe_grouped_fc1_dgrad(
+        _ptr(d_preact, torch.bfloat16, R * 2 * I, "d_preact"),
+        _ptr(w1, torch.bfloat16, E * 2 * I * H, "w1"), N, H, I, E, C,
+        _ptr(d_a, torch.bfloat16, R * H, "d_a"), _stream(stream)))
+
+
+def moe_grouped_fc2_wgrad(dy, act, sorted_slot_ids, E: int, C: int, dw2, stream=None):
+    N, H = dy.shape
+    R, I = act.shape
+    if R < E * moe_padded_capacity(C):
+        raise ValueError("act must hold E*Cp rows")
+    R = E * moe_padded_capacity(C)
+    _check("moe_grouped_fc2_wgrad", lib.moe_grouped_fc2_wgrad(
+        _ptr(dy, torch.bfloat16, N * H, "dy"), _ptr(act, torch.bfloat16, R * I, "act"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"), N, H, I, E, C,
+        _ptr(dw2, torch.bfloat16, E * H * I, "dw2"), _stream(stream)))
+
+
+def moe_grouped_fc1_wgrad(d_preact, x, sorted_slot_ids, E: int, C: int, dw1, stream=None):
+    N, H = x.shape
+    R2, I2 = d_preact.shape
+    I = I2 // 2
+    R = E * moe_padded_capacity(C)
+    if R2 < R:
+        raise ValueError("d_preact must hold E*Cp rows")
+    _check("moe_grouped_fc1_wgrad", lib.moe_grouped_fc1_wgrad(
+        _ptr(d_preact, torch.bfloat16, R * 2 * I, "d_preact"), _ptr(x, torch.bfloat16, N * H, "x"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"), N, H, I, E, C,
+        _ptr(dw1, torch.bfloat16, E * 2 * I * H, "dw1"), _stream(stream)))
+
+
+def moe_route_bwd(topk_ids, topk_probs, token_routes, d_prob, d_logits, stream=None):
+    N, K = topk_ids.shape
+    E = d_logits.shape[1]
+    R = d_prob.numel()
+    _check("moe_route_bwd", lib.moe_route_bwd(
+        _ptr(topk_ids, torch.int32, N * K, "topk_ids"),
+        _ptr(topk_probs, torch.float32, N * K, "topk_probs"),
+        _ptr(token_routes, torch.int32, N * K, "token_routes"),
+        _ptr(d_prob, torch.float32, R, "d_prob"), N, E, K, R,
+        _ptr(d_logits, torch.float32, N * E, "d_logits"), _stream(stream)))

@@ -1,0 +1,109 @@
+// Building blocks shared by the grouped GEMMs of libmoe_native (internal).
+//
+// Raw buffer descriptors whose range check turns out-of-range rows into
+// zeros, LDS DMA loads (global memory straight into LDS) with explicit
+// vector-memory waits, and the XCD-aware workgroup renumbering.
+#pragma once
+
+#include "moe_common.h"
+
+namespace moe {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (CDNA)
+// An offset past every descriptor used here (each covers < 2 GiB): a load
+// from it returns zeros without touching memory, a store to it is dropped.
+constexpr uint32_t kOob = 0x80000000u;
+
+__device__ __forceinline__ int xcd_remap(int bid, int G) {
+    const int q = G / kXcds, r = G % kXcds;
+    const int x = bid % kXcds, s = bid / kXcds;
+    return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: base, stride 0, num_records = bytes, 32-bit data format.
+// A load whose offset (everything is passed in the per-lane voffset, which the
+// range check covers) lies at or beyond `bytes` returns zeros and touches no
+// memory: this is how the sentinel row N and rows past an expert's segment
+// read as zeros.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    i32x4 r;
+    // the descriptor lives in scalar registers: every lane holds the same value
+    r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
+    r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu));
+    r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+    r.w = kRsrcWord3;
+    return r;
+}
+
+// LDS byte address of a __shared__ object (what M0 and ds_* instructions use).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+        (const __attribute__((address_space(3))) void*)p));
+}
+
+// The four descriptor words as scalars (a no-op when they already are).
+__device__ __forceinline__ i32x4 uniform(i32x4 r) {
+    r.x = __builtin_amdgcn_readfirstlane(r.x);
+    r.y = __builtin_amdgcn_readfirstlane(r.y);
+    r.z = __builtin_amdgcn_readfirstlane(r.z);
+    r.w = __builtin_amdgcn_readfirstlane(r.w);
+    return r;
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane L's data lands
+// at M0 + 16*L, so one wave fills one contiguous kilobyte.  Issued as inline
+// assembly so the compiler neither tracks it (it would otherwise wait for every
+// pending LDS-bound load before any LDS read) nor reorders it across the
+// explicit waits below ("memory" clobber).  The compiler's hazard checks do
+// not see into inline assembly, so the statement opens with the wait states
+// gfx9-family parts need before a vector-memory instruction: 5 after a VALU
+// write of an SGPR it reads (the descriptor may come from v_readfirstlane)
+// and 1 after a write of M0 that an LDS DMA reads.  STREAM marks the data
+// non-temporal (read once; the caches need not keep it).
+template <bool STREAM = false>
+__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
+    if (STREAM)
+        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
+                     :: "v"(voff), "s"(uniform(rsrc)), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                     : "memory");
+    else
+        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+                     :: "v"(voff), "s"(uniform(rsrc)), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+                     : "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are pending.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+}
+
+__device__ __forceinline__ float silu(float g) {
+    // g * sigmoid(g) = g / (1 + e^-g), e^-g = 2^(-g * log2 e)
+    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
+    return g * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// LDS layout of one stage: tile row r (ROWB = 2*BK bytes, CPR = ROWB/16
+// chunks of 8 K values) at r*ROWB; logical chunk c sits at physical chunk
+// c ^ ((r / RP) % CPR) with RP = 256/ROWB rows per 256 bytes.  An MFMA operand
+// read has 16 consecutive lanes fetch one chunk of 16 consecutive rows; with
+// 64 four-byte banks the swizzle spreads them over all 256 bytes.
+template <int BK>
+__device__ __forceinline__ uint32_t lds_off(int r, int c) {
+    constexpr int ROWB = BK * 2, CPR = ROWB / 16, RP = 256 / ROWB;
+    return static_cast<uint32_t>(r * ROWB + ((c ^ ((r / RP) % CPR)) << 4));
+}
+
+}  // namespace
+}  // namespace moe

@@ -1,0 +1,442 @@
+// Backward of the permute-free grouped FFN: data-gradient and weight-gradient
+// GEMMs.
+//
+// [PF] "Permute-Free Grouped GEMM for MoE (bf16, gfx950)":
+//   section 3  FC2 dgrad gathers the token-space gradient dy into the route
+//              buffer (here inside the A-tile loads, as the forward gathers x);
+//              FC1 dgrad's per-route input gradients are reduced to token rows
+//              by the contention-free gather-combine (combine.hip);
+//   section 5  dgrad contracts against the transposed-weight view; wgrad is
+//              expert-centric, contracts over the slot axis with an LDS fill
+//              and transpose reads, and each dW tile has exactly one owner.
+//
+// Four GEMMs, one template.  Per expert e (slots [e*Cp, (e+1)*Cp)):
+//
+//   FC2 dgrad  d_act[s, i]  = sum_h dy[row(s), h] * W2[e][h, i]
+//   FC1 dgrad  d_a[s, h]    = sum_j d_pre[s, j]   * W1[e][j, h]
+//   FC2 wgrad  dW2[e][h, i] = sum_s dy[row(s), h] * act[s, i]
+//   FC1 wgrad  dW1[e][j, h] = sum_s d_pre[s, j]   * x[row(s), h]
+//
+// with row(s) = sorted_slot_ids[s] (the sentinel N reads as a zero row).
+//
+// gfx950 design:
+//   * bf16 MFMA 32x32x16, float32 accumulators, 256x256 output tiles over 8
+//     waves, 64-deep K slabs staged through LDS by DMA (global -> LDS) rings;
+//   * the B operand is K-major in memory in all four (weights [K][N] for
+//     dgrad, route rows [slot][N] for wgrad): its stage holds one K row per
+//     LDS row and the MFMA fragments (8 consecutive K per lane) come from two
+//     ds_read_b64_tr_b16 transpose reads.  gfx950's transpose read hands lane
+//     i of a 16-lane group element i%4 of the 8-byte pieces addressed by
+//     lanes 4j + i/4 (j = 0..3); so when lane c addresses row k0 + c/4,
+//     columns n0 + 4(c%4) .. +3, lane i receives column n0 + i of rows
+//     k0 .. k0+3;
+//   * the A operand is row-major by slot for dgrad (read with ds_read_b128,
+//     like the forward) and K-major for wgrad (transpose reads again);
+//   * K-major stages swizzle their 16-byte chunks by row (chunk ^ 4*(row%4)):
+//     the four rows of one transpose read then fall on disjoint banks;
+//   * gathered rows come straight from token order through the route list;
+//     for K-major gathered operands the tokens of each slab are fetched with
+//     scalar loads (the rows change every slab);
+//   * one workgroup per output tile; consecutive tiles (same expert,
+//     neighbouring N-tiles) are renumbered onto the same XCD.
+#include <algorithm>
+#include <initializer_list>
+
+#include "gemm_common.h"
+
+namespace moe {
+namespace {
+
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+
+enum RowSrc : int {
+    kRowWeight = 0,   // row k of expert e's weight matrix
+    kRowRoute = 1,    // row s of a route-ordered buffer (the expert's segment)
+    kRowGather = 2,   // token row sorted_slot_ids[s] of a token-ordered buffer
+};
+
+struct BwdArgs {
+    const uint16_t* a;            // A source: dy (FC2) or d_pre (FC1)
+    const uint16_t* b;            // B source: W2 / W1 (dgrad), act / x (wgrad)
+    const int* sorted_slot_ids;
+    uint16_t* out;
+    int lda, ldb, ldo;            // row pitches in elements
+    int N;                        // token rows of gathered sources
+    int M, Nn, Kd;                // per-expert product: out[M, Nn] over Kd
+    int Cp;                       // slots per expert
+    int MT, NT, tiles;
+    int64_t b_estride;            // weights: elements between experts (dgrad)
+    int64_t o_estride;            // dW: elements between experts (wgrad)
+};
+
+typedef const __attribute__((address_space(4))) int* const_int_ptr;
+
+// Byte offset, within a K-major stage (rows of ROWB bytes), of the 8-byte
+// piece that lane `lane` addresses in a transpose read of the 32-wide column
+// block at column t, K rows kb .. kb+7 (read r = 0 or 1 covers kb+4r ..).
+template <int ROWB>
+__device__ __forceinline__ uint32_t tr_off(int lane, int t, int kb, int r) {
+    const int g = lane >> 4, i = lane & 15;
+    const int col = t + 16 * (g & 1) + 4 * (i & 3);
+    const int k = kb + 8 * (g >> 1) + 4 * r + (i >> 2);
+    const int lc = col >> 3, half = (col >> 2) & 1;
+    return static_cast<uint32_t>(k * ROWB + ((lc ^ (4 * (k & 3))) << 4) + half * 8);
+}
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* stage, uint32_t off0, uint32_t off1) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off1));
+    typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// WG = false: data gradient (out rows = the expert's slots, A row-major by
+//             slot, B = weights K-major);
+// WG = true:  weight gradient (out = dW[e], A and B K-major by slot).
+template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool WG, int ASRC, int BSRC>
+__global__ __launch_bounds__(WM * WN * kWave) void bwd_gemm_kernel(BwdArgs p) {
+    constexpr int NW = WM * WN;
+    constexpr int WTM = BMT / WM, WTN = BNT / WN;
+    constexpr int MI = WTM / 32, NI = WTN / 32;
+    // A row-major (dgrad): BMT rows of BK columns; K-major: BK rows of BMT.
+    constexpr int AROWB = WG ? BMT * 2 : BK * 2;
+    constexpr int BROWB = BNT * 2;
+    constexpr int A_STAGE = WG ? BK * AROWB : BMT * AROWB;
+    constexpr int B_STAGE = BK * BROWB;
+    constexpr int A_RPI = 1024 / AROWB, B_RPI = 1024 / BROWB;   // rows per DMA load
+    constexpr int A_CPR = AROWB / 16, B_CPR = BROWB / 16;       // 16-byte chunks per row
+    constexpr int A_INST = A_STAGE / 1024 / NW, B_INST = B_STAGE / 1024 / NW;
+    constexpr int LOADS = A_INST + B_INST;
+    constexpr int B_RING = NA * A_STAGE;
+    constexpr int LDS_BYTES = NA * A_STAGE + NB * B_STAGE;
+    constexpr int WAIT = NA < NB ? B_INST + (NA - 2) * LOADS : (NB - 2) * LOADS;
+    static_assert(MI >= 1 && NI >= 1 && BK == 64, "tile shape");
+    static_assert(A_INST >= 1 && B_INST >= 1 && A_STAGE % (1024 * NW) == 0 &&
+                  B_STAGE % (1024 * NW) == 0, "whole DMA blocks per wave");
+    static_assert(NA >= 2 && NB >= 2 && WAIT < 64, "stage rings");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    static_assert(!WG || (ASRC != kRowWeight && BSRC != kRowWeight), "wgrad rows are slots");
+    static_assert(WG || (ASRC != kRowWeight && BSRC == kRowWeight), "dgrad: slots x weights");
+
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int wm = wave / WN, wn = wave % WN;
+    const int half = lane >> 5;
+
+    // ---- the tile: expert, then M-tile, then N-tile (innermost)
+    int t = xcd_remap(blockIdx.x, gridDim.x);
+    const int nt = t % p.NT;
+    t /= p.NT;
+    const int mt = t % p.MT;
+    const int e = t / p.MT;
+    const int m0 = mt * BMT, n0 = nt * BNT;
+    const int seg = e * p.Cp, len = p.Cp;
+    const int KT = (p.Kd + BK - 1) / BK;
+
+    // ---- descriptors (everything outside them reads zeros)
+    const uint32_t a_rowb = static_cast<uint32_t>(p.lda) * 2u;
+    const uint32_t b_rowb = static_cast<uint32_t>(p.ldb) * 2u;
+    auto src_rsrc = [&](const uint16_t* base, int src, uint32_t rowb) {
+        if (src == kRowGather) return make_rsrc(base, static_cast<uint32_t>(p.N) * rowb);
+        if (src == kRowRoute)
+            return make_rsrc(base + static_cast<int64_t>(seg) * (rowb / 2), static_cast<uint32_t>(len) * rowb);
+        return make_rsrc(base + static_cast<int64_t>(e) * p.b_estride,
+                         static_cast<uint32_t>(p.Kd) * rowb);
+    };
+    const i32x4 ra = src_rsrc(p.a, ASRC, a_rowb);
+    const i32x4 rb = src_rsrc(p.b, BSRC, b_rowb);
+
+    // ---- DMA addressing.  Wave w's load i fills 1 KB block q = w + i*NW of
+    // the stage: RPI rows, lane L at row RPI*q + L/CPR, physical chunk L%CPR,
+    // i.e. the logical chunk the row's swizzle puts there.
+    auto dma_row = [&](int rpi, int cpr, int i) { return rpi * (wave + i * NW) + lane / cpr; };
+    // row-major A (dgrad): the forward's swizzle (chunk ^ (row/2) % 8)
+    auto rm_chunk = [&](int r) { return (lane % A_CPR) ^ ((r / (256 / AROWB)) % A_CPR); };
+    // K-major: chunk ^ 4*(row%4)
+    auto km_chunk = [&](int cpr, int r) { return (lane % cpr) ^ (4 * (r & 3)); };
+
+    // row-major gathered / route A rows are fixed for the tile
+    uint32_t a_fix[A_INST];
+    if (!WG) {
+#pragma unroll
+        for (int i = 0; i < A_INST; ++i) {
+            const int r = dma_row(A_RPI, A_CPR, i);
+            int row;
+            if (ASRC == kRowGather) {
+                const int tok = m0 + r < len ? p.sorted_slot_ids[seg + m0 + r] : p.N;
+                row = static_cast<unsigned>(tok) < static_cast<unsigned>(p.N) ? tok : p.N;
+            } else {
+                row = m0 + r;
+            }
+            a_fix[i] = static_cast<uint32_t>(row) * a_rowb + rm_chunk(r) * 16u;
+        }
+    }
+
+    // The source row of K-major row r (within slab kt) of a slot-indexed
+    // operand; the tokens of gathered rows come from scalar loads.
+    auto slot_row = [&](int src, int rpi, int cpr, int i, int kt) -> int {
+        const int base = kt * BK + rpi * (wave + i * NW);      // uniform
+        if (base >= len || kt >= KT) return -1;                 // past the segment: zeros
+        if (src == kRowRoute) return base + lane / cpr;
+        const const_int_ptr q = (const_int_ptr)(p.sorted_slot_ids) + seg + base;
+        int tok = q[0];
+#pragma unroll
+        for (int j = 1; j < 4; ++j)
+            if (j < rpi) { const int v = q[j]; tok = lane / cpr == j ? v : tok; }
+        return static_cast<unsigned>(tok) < static_cast<unsigned>(p.N) ? tok : -1;
+    };
+
+    const uint32_t lds0 = lds_addr(smem);
+    auto a_voff = [&](int i, int kt) -> uint32_t {
+        if (!WG) return kt < KT ? a_fix[i] + static_cast<uint32_t>(kt) * AROWB : kOob;
+        const int r = slot_row(ASRC, A_RPI, A_CPR, i, kt);
+        const int rr = dma_row(A_RPI, A_CPR, i);
+        return r < 0 ? kOob
+                     : static_cast<uint32_t>(r) * a_rowb + (m0 + km_chunk(A_CPR, rr) * 8) * 2u;
+    };
+    auto b_voff = [&](int i, int kt) -> uint32_t {
+        const int rr = dma_row(B_RPI, B_CPR, i);
+        int r;
+        if (WG) {
+            r = slot_row(BSRC, B_RPI, B_CPR, i, kt);
+        } else {
+            r = kt < KT ? kt * BK + rr : -1;
+        }
+        return r < 0 ? kOob : static_cast<uint32_t>(r) * b_rowb + (n0 + km_chunk(B_CPR, rr) * 8) * 2u;
+    };
+    auto issue_a = [&](int i, int kt, int stage_off) {
+        dma16(ra, a_voff(i, kt), lds0 + stage_off + (wave + i * NW) * 1024);
+    };
+    auto issue_b = [&](int i, int kt, int stage_off) {
+        dma16<!WG>(rb, b_voff(i, kt), lds0 + B_RING + stage_off + (wave + i * NW) * 1024);
+    };
+
+    floatx16 acc[MI][NI];
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+            for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
+
+    int a_read = 0, b_read = 0;
+    int a_fill = (NA - 1) * A_STAGE, b_fill = (NB - 1) * B_STAGE;
+
+    constexpr int LEAD = NA > NB ? NA : NB;
+#pragma unroll
+    for (int j = -(LEAD - 1); j < 0; ++j) {
+        if (j + NA - 1 >= 0)
+#pragma unroll
+            for (int i = 0; i < A_INST; ++i) issue_a(i, j + NA - 1, (j + NA - 1) * A_STAGE);
+        if (j + NB - 1 >= 0)
+#pragma unroll
+            for (int i = 0; i < B_INST; ++i) issue_b(i, j + NB - 1, (j + NB - 1) * B_STAGE);
+    }
+
+    constexpr int SLICES = BK / 16;
+    for (int kt = 0; kt < KT; ++kt) {
+        wait_vmcnt<WAIT>();
+        __syncthreads();
+        const lds_u8* sA = (const lds_u8*)smem + a_read;
+        const lds_u8* sB = (const lds_u8*)smem + B_RING + b_read;
+#pragma unroll
+        for (int ks = 0; ks < SLICES; ++ks) {
+            bf16x8 af[MI], bfr[NI];
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const int tm = wm * WTM + mi * 32;
+                if (WG) {
+                    af[mi] = tr_frag(sA, tr_off<AROWB>(lane, tm, ks * 16, 0),
+                                     tr_off<AROWB>(lane, tm, ks * 16, 1));
+                } else {
+                    af[mi] = *reinterpret_cast<const bf16x8*>(
+                        smem + a_read + lds_off<BK>(tm + (lane & 31), ks * 2 + half));
+                }
+            }
+#pragma unroll
+            for (int ni = 0; ni < NI; ++ni) {
+                const int tn = wn * WTN + ni * 32;
+                bfr[ni] = tr_frag(sB, tr_off<BROWB>(lane, tn, ks * 16, 0),
+                                  tr_off<BROWB>(lane, tn, ks * 16, 1));
+            }
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+            // this slice's share of the refill: slabs kt+NA-1 and kt+NB-1
+            // into the stages computed at step kt-1
+#pragma unroll
+            for (int q = ks * LOADS / SLICES; q < (ks + 1) * LOADS / SLICES; ++q) {
+                if (q < A_INST) issue_a(q, kt + NA - 1, a_fill);
+                else issue_b(q - A_INST, kt + NB - 1, b_fill);
+            }
+        }
+        const int a = a_read, b = b_read;
+        a_read = a + A_STAGE == NA * A_STAGE ? 0 : a + A_STAGE;
+        b_read = b + B_STAGE == NB * B_STAGE ? 0 : b + B_STAGE;
+        a_fill = a;
+        b_fill = b;
+    }
+
+    // ---- epilogue: lane (row l&31, half h) holds columns 8g + 4h + (0..3)
+    // of each 32-column block in acc[4g .. 4g+3]; bf16, half swap, 16-byte
+    // stores.  Rows and columns past the output get an offset beyond the
+    // descriptor: the store is dropped.
+    const int orows = WG ? p.M : len;
+    uint16_t* obase = WG ? p.out + static_cast<int64_t>(e) * p.o_estride
+                         : p.out + static_cast<int64_t>(seg) * p.ldo;
+    const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
+        obase, static_cast<short>(0), orows * p.ldo * 2, kRsrcWord3);
+#pragma unroll
+    for (int mi = 0; mi < MI; ++mi) {
+        const int row = m0 + wm * WTM + mi * 32 + (lane & 31);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+            uint32_t g[4][2];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                g[q][0] = pack_bf16x2(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1]);
+                g[q][1] = pack_bf16x2(acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
+            }
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const auto s0 = __builtin_amdgcn_permlane32_swap(g[2 * q][0], g[2 * q + 1][0], false, false);
+                const auto s1 = __builtin_amdgcn_permlane32_swap(g[2 * q][1], g[2 * q + 1][1], false, false);
+                u32x4 d;
+                d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
+                const int col = n0 + wn * WTN + ni * 32 + 16 * q + 8 * half;
+                const uint32_t off = row < orows && col < p.Nn
+                    ? (static_cast<uint32_t>(row) * p.ldo + col) * 2u : kOob;
+                __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
+            }
+        }
+    }
+    wait_vmcnt<0>();   // no DMA may still be writing LDS when the workgroup ends
+}
+
+template <bool WG, int ASRC, int BSRC>
+int launch_bwd(BwdArgs a, int E, hipStream_t s) {
+    constexpr int BMT = 256, BNT = 256, WM = 2, WN = 4, BK = 64, NA = 2, NB = 3;
+    a.MT = ((WG ? a.M : a.Cp) + BMT - 1) / BMT;
+    a.NT = (a.Nn + BNT - 1) / BNT;
+    const int64_t tiles = static_cast<int64_t>(E) * a.MT * a.NT;
+    if (tiles > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    a.tiles = static_cast<int>(tiles);
+    bwd_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, WG, ASRC, BSRC>
+        <<<a.tiles, WM * WN * kWave, 0, s>>>(a);
+    return MOE_OK;
+}
+
+// Host checks shared by the backward GEMM entry points (the forward's
+// envelope; 32-bit buffer offsets inside the kernels).
+int check_bwd(int64_t N, int32_t H, int32_t I, int32_t E, int64_t C, int* Cp) {
+    if (N < 0 || E < 1 || C < 0) return MOE_ERR_INVALID_ARG;
+    int st = check_dims(H, I);
+    if (st != MOE_OK) return st;
+    if (N > kMaxN || E > kMaxE) return MOE_ERR_UNSUPPORTED;
+    const int64_t Cp64 = moe_padded_capacity(C);
+    if (Cp64 < 0) return MOE_ERR_UNSUPPORTED;
+    const int64_t big = static_cast<int64_t>(1) << 31;
+    if (static_cast<int64_t>(E) * Cp64 > INT32_MAX || (N + 1) * H * 2 >= big ||
+        Cp64 * std::max(H, 2 * I) * 2 >= big || static_cast<int64_t>(2) * I * H * 2 >= big)
+        return MOE_ERR_UNSUPPORTED;
+    *Cp = static_cast<int>(Cp64);
+    return MOE_OK;
+}
+
+int check_ptrs16(std::initializer_list<const void*> ptrs) {
+    for (const void* q : ptrs) {
+        if (!q) return MOE_ERR_INVALID_ARG;
+        if (!aligned16(q)) return MOE_ERR_MISALIGNED;
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_grouped_fc2_dgrad(const uint16_t* dy, const uint16_t* w2,
+                                     const int32_t* sorted_slot_ids, int64_t N, int32_t H,
+                                     int32_t I, int32_t E, int64_t C, uint16_t* d_act,
+                                     hipStream_t stream) {
+    using namespace moe;
+    int Cp = 0;
+    int st = check_bwd(N, H, I, E, C, &Cp);
+    if (st != MOE_OK) return st;
+    if (N == 0 || C == 0) return MOE_OK;
+    st = check_ptrs16({dy, w2, sorted_slot_ids, d_act});
+    if (st != MOE_OK) return st;
+    BwdArgs a{};
+    a.a = dy; a.b = w2; a.sorted_slot_ids = sorted_slot_ids; a.out = d_act;
+    a.lda = H; a.ldb = I; a.ldo = I; a.N = static_cast<int>(N);
+    a.M = Cp; a.Nn = I; a.Kd = H; a.Cp = Cp;
+    a.b_estride = static_cast<int64_t>(H) * I;
+    st = launch_bwd<false, kRowGather, kRowWeight>(a, E, stream);
+    return st != MOE_OK ? st : launch_status();
+}
+
+extern "C" int moe_grouped_fc1_dgrad(const uint16_t* d_preact, const uint16_t* w1, int64_t N,
+                                     int32_t H, int32_t I, int32_t E, int64_t C, uint16_t* d_a,
+                                     hipStream_t stream) {
+    using namespace moe;
+    int Cp = 0;
+    int st = check_bwd(N, H, I, E, C, &Cp);
+    if (st != MOE_OK) return st;
+    if (N == 0 || C == 0) return MOE_OK;
+    st = check_ptrs16({d_preact, w1, d_a});
+    if (st != MOE_OK) return st;
+    BwdArgs a{};
+    a.a = d_preact; a.b = w1; a.out = d_a;
+    a.lda = 2 * I; a.ldb = H; a.ldo = H; a.N = static_cast<int>(N);
+    a.M = Cp; a.Nn = H; a.Kd = 2 * I; a.Cp = Cp;
+    a.b_estride = static_cast<int64_t>(2) * I * H;
+    st = launch_bwd<false, kRowRoute, kRowWeight>(a, E, stream);
+    return st != MOE_OK ? st : launch_status();
+}
+
+extern "C" int moe_grouped_fc2_wgrad(const uint16_t* dy, const uint16_t* act,
+                                     const int32_t* sorted_slot_ids, int64_t N, int32_t H,
+                                     int32_t I, int32_t E, int64_t C, uint16_t* dw2,
+                                     hipStream_t stream) {
+    using namespace moe;
+    int Cp = 0;
+    int st = check_bwd(N, H, I, E, C, &Cp);
+    if (st != MOE_OK) return st;
+    if (N == 0 || C == 0) return MOE_OK;   // nothing routed: dW2 is left as it was
+    st = check_ptrs16({dy, act, sorted_slot_ids, dw2});
+    if (st != MOE_OK) return st;
+    BwdArgs a{};
+    a.a = dy; a.b = act; a.sorted_slot_ids = sorted_slot_ids; a.out = dw2;
+    a.lda = H; a.ldb = I; a.ldo = I; a.N = static_cast<int>(N);
+    a.M = H; a.Nn = I; a.Kd = Cp; a.Cp = Cp;
+    a.o_estride = static_cast<int64_t>(H) * I;
+    st = launch_bwd<true, kRowGather, kRowRoute>(a, E, stream);
+    return st != MOE_OK ? st : launch_status();
+}
+
+extern "C" int moe_grouped_fc1_wgrad(const uint16_t* d_preact, const uint16_t* x,
+                                     const int32_t* sorted_slot_ids, int64_t N, int32_t H,
+                                     int32_t I, int32_t E, int64_t C, uint16_t* dw1,
+                                     hipStream_t stream) {
+    using namespace moe;
+    int Cp = 0;
+    int st = check_bwd(N, H, I, E, C, &Cp);
+    if (st != MOE_OK) return st;
+    if (N == 0 || C == 0) return MOE_OK;
+    st = check_ptrs16({d_preact, x, sorted_slot_ids, dw1});
+    if (st != MOE_OK) return st;
+    BwdArgs a{};
+    a.a = d_preact; a.b = x; a.sorted_slot_ids = sorted_slot_ids; a.out = dw1;
+    a.lda = 2 * I; a.ldb = H; a.ldo = H; a.N = static_cast<int>(N);
+    a.M = 2 * I; a.Nn = H; a.Kd = Cp; a.Cp = Cp;
+    a.o_estride = static_cast<int64_t>(2) * I * H;
+    st = launch_bwd<true, kRowRoute, kRowGather>(a, E, stream);
+    return st != MOE_OK ? st : launch_status();
+}

@@ -30,20 +30,11 @@
 #include <cmath>
 #include <initializer_list>
 
-#include "moe_common.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float floatx16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kXcds = 8;         // MI355X: 8 XCDs, workgroups dealt round-robin
-constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (CDNA)
-// An offset past every descriptor used here (each covers < 2 GiB): a load
-// from it returns zeros without touching memory, a store to it is dropped.
-constexpr uint32_t kOob = 0x80000000u;
 constexpr int kKRotate = 5;      // K slabs between the starting slabs of consecutive experts
 
 struct FfnArgs {
@@ -52,6 +43,7 @@ struct FfnArgs {
     const int* sorted_slot_ids;   // FC1 only
     const float* slot_probs;      // FC1 only
     uint16_t* out;                // FC1: act [E*Cp, I]; FC2: route_out [E*Cp, H]
+    uint16_t* preact;             // FC1 only, may be null: raw [gate | up] [E*Cp, 2I]
     int N;                        // tokens (FC1 sentinel row)
     int Kdim;                     // contraction length: FC1 H, FC2 I
     int ncols;                    // output columns: FC1 I, FC2 H
@@ -68,91 +60,6 @@ struct FfnArgs {
     int R;                        // slots of the route list (its static bound)
 };
 
-__device__ __forceinline__ int xcd_remap(int bid, int G) {
-    const int q = G / kXcds, r = G % kXcds;
-    const int x = bid % kXcds, s = bid / kXcds;
-    return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
-}
-
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-
-// Raw buffer descriptor: base, stride 0, num_records = bytes, 32-bit data format.
-// A load whose offset (everything is passed in the per-lane voffset, which the
-// range check covers) lies at or beyond `bytes` returns zeros and touches no
-// memory: this is how the sentinel row N and rows past an expert's segment
-// read as zeros.
-__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t bytes) {
-    const uint64_t a = reinterpret_cast<uint64_t>(base);
-    i32x4 r;
-    // the descriptor lives in scalar registers: every lane holds the same value
-    r.x = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a)));
-    r.y = __builtin_amdgcn_readfirstlane(static_cast<int>(static_cast<uint32_t>(a >> 32) & 0xFFFFu));
-    r.z = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
-    r.w = kRsrcWord3;
-    return r;
-}
-
-// LDS byte address of a __shared__ object (what M0 and ds_* instructions use).
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-        (const __attribute__((address_space(3))) void*)p));
-}
-
-// The four descriptor words as scalars (a no-op when they already are).
-__device__ __forceinline__ i32x4 uniform(i32x4 r) {
-    r.x = __builtin_amdgcn_readfirstlane(r.x);
-    r.y = __builtin_amdgcn_readfirstlane(r.y);
-    r.z = __builtin_amdgcn_readfirstlane(r.z);
-    r.w = __builtin_amdgcn_readfirstlane(r.w);
-    return r;
-}
-
-// 16 bytes per lane from global memory straight into LDS: lane L's data lands
-// at M0 + 16*L, so one wave fills one contiguous kilobyte.  Issued as inline
-// assembly so the compiler neither tracks it (it would otherwise wait for every
-// pending LDS-bound load before any LDS read) nor reorders it across the
-// explicit waits below ("memory" clobber).  The compiler's hazard checks do
-// not see into inline assembly, so the statement opens with the wait states
-// gfx9-family parts need before a vector-memory instruction: 5 after a VALU
-// write of an SGPR it reads (the descriptor may come from v_readfirstlane)
-// and 1 after a write of M0 that an LDS DMA reads.  STREAM marks the data
-// non-temporal (read once; the caches need not keep it).
-template <bool STREAM = false>
-__device__ __forceinline__ void dma16(i32x4 rsrc, uint32_t voff, uint32_t lds) {
-    if (STREAM)
-        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen nt lds"
-                     :: "v"(voff), "s"(uniform(rsrc)), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
-                     : "memory");
-    else
-        asm volatile("s_nop 4\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
-                     :: "v"(voff), "s"(uniform(rsrc)), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
-                     : "memory");
-}
-
-// Wait until at most N of this wave's vector-memory operations are pending.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
-}
-
-__device__ __forceinline__ float silu(float g) {
-    // g * sigmoid(g) = g / (1 + e^-g), e^-g = 2^(-g * log2 e)
-    const float e = __builtin_amdgcn_exp2f(-g * 1.4426950408889634f);
-    return g * __builtin_amdgcn_rcpf(1.0f + e);
-}
-
-// LDS layout of one stage: tile row r (ROWB = 2*BK bytes, CPR = ROWB/16
-// chunks of 8 K values) at r*ROWB; logical chunk c sits at physical chunk
-// c ^ ((r / RP) % CPR) with RP = 256/ROWB rows per 256 bytes.  An MFMA operand
-// read has 16 consecutive lanes fetch one chunk of 16 consecutive rows; with
-// 64 four-byte banks the swizzle spreads them over all 256 bytes.
-template <int BK>
-__device__ __forceinline__ uint32_t lds_off(int r, int c) {
-    constexpr int ROWB = BK * 2, CPR = ROWB / 16, RP = 256 / ROWB;
-    return static_cast<uint32_t>(r * ROWB + ((c ^ ((r / RP) % CPR)) << 4));
-}
-
 // One persistent workgroup per resident slot walks the tiles r*G + slot
 // (G workgroups, slot = the XCD-aware renumbering of its id), with one
 // continuous pair of LDS rings: the last steps of a tile already stream the
@@ -164,7 +71,8 @@ __device__ __forceinline__ uint32_t lds_off(int r, int c) {
 // runs of 4, so SwiGLU pairs and the routing probability live in the lane and
 // a swap of lane halves leaves 8 consecutive bf16 columns per lane for one
 // 16-byte store.
-template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1, bool DYN>
+template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1, bool DYN,
+          bool SAVE = false>
 __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BMT / WM;
@@ -181,7 +89,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     constexpr int B_INST = BNT / RPI / NW;
     constexpr int LOADS = A_INST + B_INST;                 // per wave per K slab
     constexpr int OUT_COLS = FC1 ? BNT / 2 : BNT;          // output columns of a tile
-    constexpr int STORES = FC1 ? MI * NI : 2 * MI * NI;    // 16-byte stores per lane per tile
+    // 16-byte stores per lane per tile (FC1 with SAVE also stores the raw
+    // gate and up columns, the pre-activation the backward keeps)
+    constexpr int STORES = FC1 ? (SAVE ? 3 : 1) * MI * NI : 2 * MI * NI;
+    static_assert(FC1 || !SAVE, "only FC1 has a pre-activation");
     constexpr int LDS_BYTES = NA * A_STAGE + NB * B_STAGE;
     // Step j issues A(j+NA-1) then B(j+NB-1); vector-memory operations retire
     // in issue order.  Before computing slab kt, the newer of A(kt) and B(kt)
@@ -566,6 +477,9 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
             p.out + static_cast<int64_t>(cur.seg) * p.ncols, static_cast<short>(0),
             cur.len * p.ncols * 2, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
+            SAVE ? p.preact + static_cast<int64_t>(cur.seg) * 2 * p.ncols : p.out, static_cast<short>(0),
+            SAVE ? cur.len * p.ncols * 4 : 0, kRsrcWord3);
 #pragma unroll
         for (int mi = 0; mi < MI; ++mi) {
             const int row = cur.m0 + wm * WTM + mi * 32 + (lane & 31);   // slot within the expert
@@ -588,9 +502,34 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
                     const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
                     d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
                     const int col = cur.nt * OUT_COLS + (wn * WTN + ni * 32) / 2 + 8 * half;
-                    const uint32_t off = row < cur.len && col < p.ncols
-                        ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
+                    const bool live = row < cur.len && col < p.ncols;
+                    const uint32_t off = live ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
                     __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
+                    if (SAVE) {
+                        // the same columns of the raw gate (acc[0..7]) and up
+                        // (acc[8..15]) rows, at col and I + col of the row
+                        const floatx16& v = acc[mi][ni];
+                        uint32_t gx[2], gy[2], ux[2], uy[2];
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            gx[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+                            gy[q] = pack_bf16x2(v[2 * q + 4], v[2 * q + 5]);
+                            ux[q] = pack_bf16x2(v[2 * q + 8], v[2 * q + 9]);
+                            uy[q] = pack_bf16x2(v[2 * q + 12], v[2 * q + 13]);
+                        }
+                        const auto g0 = __builtin_amdgcn_permlane32_swap(gx[0], gy[0], false, false);
+                        const auto g1 = __builtin_amdgcn_permlane32_swap(gx[1], gy[1], false, false);
+                        const auto u0 = __builtin_amdgcn_permlane32_swap(ux[0], uy[0], false, false);
+                        const auto u1 = __builtin_amdgcn_permlane32_swap(ux[1], uy[1], false, false);
+                        u32x4 dg, du;
+                        dg[0] = g0[0]; dg[1] = g1[0]; dg[2] = g0[1]; dg[3] = g1[1];
+                        du[0] = u0[0]; du[1] = u1[0]; du[2] = u0[1]; du[3] = u1[1];
+                        const uint32_t poff = live
+                            ? (static_cast<uint32_t>(row) * 2u * p.ncols + col) * 2u : kOob;
+                        __builtin_amdgcn_raw_buffer_store_b128(dg, prsrc, poff, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            du, prsrc, live ? poff + static_cast<uint32_t>(p.ncols) * 2u : kOob, 0, 0);
+                    }
                 } else {
                     uint32_t g[4][2];
 #pragma unroll
@@ -646,10 +585,11 @@ int device_cus() {
     return n;
 }
 
-template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1, bool DYN>
+template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1, bool DYN,
+          bool SAVE = false>
 void launch_persistent(const FfnArgs& a, hipStream_t s) {
     constexpr int threads = WM * WN * kWave;
-    auto* k = ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, FC1, DYN>;
+    auto* k = ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, FC1, DYN, SAVE>;
     static std::atomic<int> occupancy{0};   // workgroups per CU (LDS and registers decide it)
     int occ = occupancy.load(std::memory_order_relaxed);
     if (occ == 0) {
@@ -676,7 +616,8 @@ int launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s, bool dyn = false) {
         if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, true>(a, s);
         else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, true>(a, s);
     } else {
-        if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false>(a, s);
+        if (fc1 && a.preact) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false, true>(a, s);
+        else if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false>(a, s);
         else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, false>(a, s);
     }
     return MOE_OK;
@@ -789,6 +730,24 @@ extern "C" int moe_grouped_fc1_swiglu(const uint16_t* x, const uint16_t* w1,
     st = check_ptrs({x, w1, sorted_slot_ids, slot_probs, act});
     if (st != MOE_OK) return st;
     st = launch(fc1_args(x, w1, sorted_slot_ids, slot_probs, N, H, I, Cp, act), true, E, stream);
+    return st != MOE_OK ? st : launch_status();
+}
+
+extern "C" int moe_grouped_fc1_swiglu_save(const uint16_t* x, const uint16_t* w1,
+                                           const int32_t* sorted_slot_ids, const float* slot_probs,
+                                           int64_t N, int32_t H, int32_t I, int32_t E, int64_t C,
+                                           uint16_t* act, uint16_t* preact, hipStream_t stream) {
+    using namespace moe;
+    int Cp = 0;
+    int st = check_ffn(N, H, I, E, C, &Cp);
+    if (st != MOE_OK) return st;
+    if (static_cast<int64_t>(Cp) * I * 4 >= (static_cast<int64_t>(1) << 31)) return MOE_ERR_UNSUPPORTED;
+    if (N == 0 || C == 0) return MOE_OK;
+    st = check_ptrs({x, w1, sorted_slot_ids, slot_probs, act, preact});
+    if (st != MOE_OK) return st;
+    FfnArgs a = fc1_args(x, w1, sorted_slot_ids, slot_probs, N, H, I, Cp, act);
+    a.preact = preact;
+    st = launch(a, true, E, stream);
     return st != MOE_OK ? st : launch_status();
 }
 

@@ -77,6 +77,88 @@ class MoEBuffers:
         nat.moe_gather_combine(self.route_out, self.token_routes, self.y, stream)
 
 
+class MoEBackwardBuffers:
+    """Device buffers for the backward of one fixed-capacity layer, next to
+    the forward's MoEBuffers (whose routing state and route list it reuses).
+
+    Training step on one stream:
+        fwd_save (forward FC1 also storing the 2I pre-activation), fc2,
+        combine; then backward(dy): FC2 dgrad -> SwiGLU recompute + backward
+        -> FC1 dgrad -> gather-combine (dx) -> both weight gradients ->
+        router-logit gradient.
+    """
+
+    def __init__(self, fwd: MoEBuffers):
+        self.f = fwd
+        R, N, H, I, E = fwd.R, fwd.N, fwd.H, fwd.I, fwd.E
+        dev = fwd.act.device
+        bf16, f32 = torch.bfloat16, torch.float32
+
+        def z(shape, dt):
+            return torch.zeros(shape, dtype=dt, device=dev)
+
+        self.preact = z((R, 2 * I), bf16)
+        self.d_act = z((R, I), bf16)
+        self.act_re = z((R, I), bf16)
+        self.d_preact = z((R, 2 * I), bf16)
+        self.d_prob = z((R,), f32)
+        self.d_a = z((R, H), bf16)
+        self.dx = z((N, H), bf16)
+        self.dw1 = z((E, 2 * I, H), bf16)
+        self.dw2 = z((E, H, I), bf16)
+        self.d_logits = z((N, E), f32)
+
+    def fc1_swiglu_save(self, x, w1, stream=None):
+        f = self.f
+        nat.moe_grouped_fc1_swiglu_save(x, w1, f.sorted_slot_ids, f.slot_probs, f.C, f.act,
+                                        self.preact, stream)
+
+    def forward(self, logits, x, w1, w2, stream=None):
+        """The forward, keeping the pre-activation for the backward."""
+        f = self.f
+        f.route_capacity_align(logits, stream)
+        self.fc1_swiglu_save(x, w1, stream)
+        f.fc2(w2, stream)
+        f.combine(stream)
+        return f.y
+
+    def fc2_dgrad(self, dy, w2, stream=None):
+        nat.moe_grouped_fc2_dgrad(dy, w2, self.f.sorted_slot_ids, self.f.C, self.d_act, stream)
+
+    def swiglu_bwd(self, stream=None):
+        nat.moe_swiglu_bwd(self.preact, self.d_act, self.f.slot_probs, self.act_re,
+                           self.d_preact, self.d_prob, stream)
+
+    def fc1_dgrad(self, w1, stream=None):
+        nat.moe_grouped_fc1_dgrad(self.d_preact, w1, self.f.N, self.f.C, self.d_a, stream)
+
+    def dx_combine(self, stream=None):
+        nat.moe_gather_combine(self.d_a, self.f.token_routes, self.dx, stream)
+
+    def fc2_wgrad(self, dy, stream=None):
+        nat.moe_grouped_fc2_wgrad(dy, self.act_re, self.f.sorted_slot_ids, self.f.E, self.f.C,
+                                  self.dw2, stream)
+
+    def fc1_wgrad(self, x, stream=None):
+        nat.moe_grouped_fc1_wgrad(self.d_preact, x, self.f.sorted_slot_ids, self.f.E, self.f.C,
+                                  self.dw1, stream)
+
+    def route_bwd(self, stream=None):
+        f = self.f
+        nat.moe_route_bwd(f.topk_ids, f.topk_probs, f.token_routes, self.d_prob, self.d_logits,
+                          stream)
+
+    def backward(self, dy, x, w1, w2, stream=None):
+        """All backward steps in order; results in dx, dw1, dw2, d_logits."""
+        self.fc2_dgrad(dy, w2, stream)
+        self.swiglu_bwd(stream)
+        self.fc1_dgrad(w1, stream)
+        self.dx_combine(stream)
+        self.fc2_wgrad(dy, stream)
+        self.fc1_wgrad(x, stream)
+        self.route_bwd(stream)
+
+
 def forward(buf: MoEBuffers, logits, x, w1, w2, stream=None):
     """Steps 1-5 on one stream; returns buf.y (bf16 [N, H])."""
     buf.route_capacity_align(logits, stream)

@@ -21,6 +21,9 @@ Streams:
   which is harmless because the oracle always reads the very tensors the GPU
   path consumes (copied to the host).
 
+Backward: the upstream gradient dy of the layer output is bf16 ~ N(0, 1),
+[N, H], drawn like x with seed*1000 + 5.
+
 Skewed routing: logits + alpha * rank_e^(-1.1), rank a seeded permutation of
 1..E (numpy, SeedSequence([seed, 4])).  alpha is a parameter; the value that
 makes the busiest expert carry about 1.35x its balanced share is stored
@@ -126,6 +129,15 @@ def make_tensors(w: Workload, device="cpu", skew_alpha: float | None = None,
         g.manual_seed(w.seed * 1000 + 3)
         out["w2"] = _normal_bf16((w.E, w.H, w.I), 0.02, g, device)
     return out
+
+
+def make_dy(w: Workload, device="cpu") -> torch.Tensor:
+    """Upstream gradient of the layer output for the backward: bf16 [N, H]
+    ~ N(0, 1), torch's generator on ``device`` seeded with seed*1000 + 5."""
+    device = torch.device(device)
+    g = torch.Generator(device=device)
+    g.manual_seed(w.seed * 1000 + 5)
+    return _normal_bf16((w.N, w.H), 1.0, g, device)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:

@@ -44,7 +44,12 @@ from .moe import (  # noqa: F401
 from .backward import (  # noqa: F401
     backward,
     expert_backward,
+    fc1_dgrad,
     fc1_preact,
+    fc1_preact_slots,
+    fc1_wgrad,
+    fc2_dgrad,
+    fc2_wgrad,
     grouped_ffn_backward,
     route_backward,
     swiglu_backward,

@@ -183,6 +183,70 @@ def grouped_ffn_backward(x, dy, w1, w2, sorted_slot_ids, slot_probs, E: int, Cp:
     return out
 
 
+# ---------------------------------------------------------------------------
+# The same steps one at a time over the whole route list, each fed whatever
+# inputs the caller has (the GPU's own intermediates in the step-wise parity
+# tests).  Chained in order they reproduce grouped_ffn_backward exactly.
+# ---------------------------------------------------------------------------
+
+def _gather_rows(src, sorted_slot_ids, lo, hi):
+    """Rows sorted_slot_ids[lo:hi] of a token-ordered float64 array (zeros
+    for the sentinel)."""
+    rows = np.asarray(sorted_slot_ids)[lo:hi]
+    out = np.zeros((hi - lo, src.shape[1]))
+    real = rows < src.shape[0]
+    out[real] = src[rows[real]]
+    return out
+
+
+def fc2_dgrad(dy, w2, sorted_slot_ids, E: int, Cp: int):
+    """d_act[s] = bf16(dy[row(s)] @ W2[e]) for every slot (bf16 bits)."""
+    dyf = _f64(dy)
+    I = np.asarray(w2[0]).shape[1]
+    out = np.zeros((E * Cp, I))
+    for e in range(E):
+        out[e * Cp:(e + 1) * Cp] = _gather_rows(dyf, sorted_slot_ids, e * Cp, (e + 1) * Cp) @ _f64(w2[e])
+    return f64_to_bf16_bits(out)
+
+
+def fc1_dgrad(d_preact, w1, E: int, Cp: int):
+    """d_a[s] = bf16(d_preact[s] @ W1[e]) for every slot (bf16 bits)."""
+    dp = _f64(d_preact)
+    H = np.asarray(w1[0]).shape[1]
+    out = np.zeros((E * Cp, H))
+    for e in range(E):
+        out[e * Cp:(e + 1) * Cp] = dp[e * Cp:(e + 1) * Cp] @ _f64(w1[e])
+    return f64_to_bf16_bits(out)
+
+
+def fc2_wgrad(dy, act, sorted_slot_ids, E: int, Cp: int):
+    """dW2[e] = bf16(sum over e's slots of dy[row(s)]^T act[s]) (bf16 bits)."""
+    dyf = _f64(dy)
+    af = _f64(act)
+    out = np.stack([_gather_rows(dyf, sorted_slot_ids, e * Cp, (e + 1) * Cp).T @ af[e * Cp:(e + 1) * Cp]
+                    for e in range(E)])
+    return f64_to_bf16_bits(out)
+
+
+def fc1_wgrad(d_preact, x, sorted_slot_ids, E: int, Cp: int):
+    """dW1[e] = bf16(sum over e's slots of d_preact[s]^T x[row(s)]) (bf16 bits)."""
+    dp = _f64(d_preact)
+    xf = _f64(x)
+    out = np.stack([dp[e * Cp:(e + 1) * Cp].T @ _gather_rows(xf, sorted_slot_ids, e * Cp, (e + 1) * Cp)
+                    for e in range(E)])
+    return f64_to_bf16_bits(out)
+
+
+def fc1_preact_slots(x, w1, sorted_slot_ids, E: int, Cp: int):
+    """The saved pre-activation of every slot: bf16(x[row(s)] @ W1[e]^T)."""
+    xf = _f64(x)
+    I2 = np.asarray(w1[0]).shape[0]
+    out = np.zeros((E * Cp, I2))
+    for e in range(E):
+        out[e * Cp:(e + 1) * Cp] = _gather_rows(xf, sorted_slot_ids, e * Cp, (e + 1) * Cp) @ _f64(w1[e]).T
+    return f64_to_bf16_bits(out)
+
+
 def route_backward(ids, probs, token_routes, d_prob_slots, E: int, exact: bool = False):
     """Gradient of the router logits through the softmax over the top K.
 

@@ -23,7 +23,9 @@ def test_every_declared_symbol_is_exported():
                           "moe_grouped_ffn_fwd_dropless", "moe_grouped_fc1_swiglu_dropless",
                           "moe_grouped_fc2_dropless",
                           "moe_grouped_ffn_fwd", "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
-                          "moe_gather_combine"}
+                          "moe_gather_combine", "moe_grouped_fc1_swiglu_save",
+                          "moe_grouped_fc2_dgrad", "moe_swiglu_bwd", "moe_grouped_fc1_dgrad",
+                          "moe_grouped_fc2_wgrad", "moe_grouped_fc1_wgrad", "moe_route_bwd"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -151,3 +153,32 @@ def test_combine_validation():
     assert f(ALIGNED, ALIGNED, 16, 2, 72, 128, ALIGNED, NUL) == UNSUPPORTED
     assert f(ALIGNED, MIS, 16, 2, 64, 128, ALIGNED, NUL) == MISALIGNED
     assert f(NUL, NUL, 0, 2, 64, 0, NUL, NUL) == OK
+
+
+def test_backward_validation():
+    A = ALIGNED
+    f = lib.moe_grouped_fc1_swiglu_save
+    assert f(A, A, A, A, 16, 100, 64, 4, 8, A, A, NUL) == UNSUPPORTED               # H % 64
+    assert f(A, A, A, A, 16, 64, 64, 4, 8, A, MIS, NUL) == MISALIGNED
+    assert f(A, A, A, A, 16, 64, 64, 4, 8, A, NUL, NUL) == INVALID
+    assert f(*([NUL] * 4), 0, 64, 64, 4, 0, NUL, NUL, NUL) == OK
+    for g in (lib.moe_grouped_fc2_dgrad, lib.moe_grouped_fc2_wgrad, lib.moe_grouped_fc1_wgrad):
+        assert g(A, A, A, 16, 64, 96, 4, 8, A, NUL) == UNSUPPORTED                   # I % 64
+        assert g(A, A, A, -1, 64, 64, 4, 8, A, NUL) == INVALID                        # N < 0
+        assert g(A, A, NUL, 16, 64, 64, 4, 8, A, NUL) == INVALID
+        assert g(A, A, A, 16, 64, 64, 4, 8, MIS, NUL) == MISALIGNED
+        assert g(NUL, NUL, NUL, 0, 64, 64, 4, 0, NUL, NUL) == OK
+    g = lib.moe_grouped_fc1_dgrad
+    assert g(A, A, 16, 64, 64, 2048, 8, A, NUL) == UNSUPPORTED                         # E > 1024
+    assert g(A, NUL, 16, 64, 64, 4, 8, A, NUL) == INVALID
+    assert g(NUL, NUL, 0, 64, 64, 4, 0, NUL, NUL) == OK
+    h = lib.moe_swiglu_bwd
+    assert h(A, A, A, 128, 100, A, A, A, NUL) == UNSUPPORTED                           # I % 64
+    assert h(A, A, A, -1, 64, A, A, A, NUL) == INVALID
+    assert h(A, A, A, 128, 64, A, A, MIS, NUL) == MISALIGNED
+    assert h(NUL, NUL, NUL, 0, 64, NUL, NUL, NUL, NUL) == OK
+    r = lib.moe_route_bwd
+    assert r(A, A, A, A, 16, 4, 5, 128, A, NUL) == INVALID                             # K > E
+    assert r(A, A, A, A, 16, 4, 2, 128, NUL, NUL) == INVALID
+    assert r(A, A, A, A, 16, 2048, 2, 128, A, NUL) == UNSUPPORTED
+    assert r(NUL, NUL, NUL, NUL, 0, 4, 2, 0, NUL, NUL) == OK

@@ -199,3 +199,25 @@ def test_swiglu_backward_finite_differences(seed):
     _, d_pre, d_prob = oracle.swiglu_backward(h, da, p, exact=True)
     np.testing.assert_allclose(d_pre, _fd(act_sum, h), rtol=1e-6, atol=1e-8)
     np.testing.assert_allclose(d_prob, _fd(act_sum, p), rtol=1e-6, atol=1e-8)
+
+
+def test_stepwise_functions_chain_to_grouped_backward():
+    """The one-step-at-a-time functions, chained, give grouped_ffn_backward's
+    results bit for bit (they are what the GPU parity tests feed)."""
+    w = moe_inputs.WORKLOADS["tiny_n64_h64_e4_k2"]
+    T = moe_inputs.make_tensors(w, "cpu")
+    x, w1, w2 = (moe_inputs.bf16_bits(T[k]) for k in ("x", "w1", "w2"))
+    fwd = oracle.forward(T["logits"].numpy(), x, w1, w2, w.K, w.F)
+    dy = moe_inputs.bf16_bits(moe_inputs.make_dy(w, "cpu"))
+    ssi, sp, E, Cp = fwd["sorted_slot_ids"], fwd["slot_probs"], w.E, fwd["Cp"]
+    G = oracle.grouped_ffn_backward(x, dy, w1, w2, ssi, sp, E, Cp)
+    pre = oracle.fc1_preact_slots(x, w1, ssi, E, Cp)
+    assert np.array_equal(pre, G["preact"])
+    d_act = oracle.fc2_dgrad(dy, w2, ssi, E, Cp)
+    assert np.array_equal(d_act, G["d_act"])
+    act, d_pre, d_prob = oracle.swiglu_backward(pre, d_act, sp)
+    assert np.array_equal(act, G["act"]) and np.array_equal(d_pre, G["d_preact"])
+    assert np.array_equal(d_prob, G["d_prob"])
+    assert np.array_equal(oracle.fc1_dgrad(d_pre, w1, E, Cp), G["d_a"])
+    assert np.array_equal(oracle.fc2_wgrad(dy, act, ssi, E, Cp), G["dw2"])
+    assert np.array_equal(oracle.fc1_wgrad(d_pre, x, ssi, E, Cp), G["dw1"])

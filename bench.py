@@ -16,11 +16,14 @@ Timed regions (all on the stream the library launches on):
   3. cpu_baseline: the CPU oracle on the same inputs (median of a few full
      forwards), rank 0 only.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant capacity|dropless]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--variant capacity|dropless|backward]
 
 --variant dropless measures the dropless form instead (every route kept,
 block-padded segments, the extent a device scalar): its own JSON line, with
-the algorithmic work taken at the real padded extent.
+the algorithmic work taken at the real padded extent.  --variant backward
+measures the layer's training step (forward keeping the pre-activation, then
+the backward for a seeded dy), with the roofline of the slowest backward
+kernel.
 """
 
 from __future__ import annotations
@@ -83,27 +86,6 @@ def algorithmic_bytes_dropless(w, X, Rd, BM):
     }
 
 
-def roofline_fc1(flops, nbytes, us, traffic):
-    """Roofline of the dominant kernel (FC1).  Its bound is whichever resource
-    needs the longer time at peak: at C=256 the weight stream (HBM) outlasts
-    the MFMA work, so `achieved` is algorithmic bytes per launch / launch time
-    against 8 TB/s; the MFMA figures are kept beside it."""
-    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
-    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
-    gbs = nbytes / (us * 1e-6) / 1e9
-    tflops = flops / (us * 1e-6) / 1e12
-    common = {"kernel": "fc1_swiglu (gather-in-GEMM FC1 + SwiGLU*prob)", "traffic": traffic,
-              "algorithmic_bytes": nbytes, "flops": flops, "launch_us": us,
-              "arithmetic_intensity": flops / nbytes,
-              "attainable_frac": max(t_hbm, t_mfma) / (us * 1e-6)}
-    if t_hbm >= t_mfma:
-        return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": gbs / PEAK_HBM_GBS, "mfma_tflops": tflops,
-                "mfma_frac": tflops / PEAK_BF16_TFLOPS, **common}
-    return {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": tflops / PEAK_BF16_TFLOPS, "hbm_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, **common}
-
-
 def pmc_traffic(launch_bytes_unit):
     """FC1's HBM traffic per launch from the committed rocprofv3 counter summary,
     scaled by the copy-kernel calibration; None if absent or taken on other code."""
@@ -143,12 +125,7 @@ def cpu_baseline(T, w, forwards, min_seconds=12.0, dropless=False):
     import numpy as np
     import moe_inputs
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
-        blas = ",".join(sorted({p.get("internal_api", "?") for p in threadpool_info() if p.get("user_api") == "blas"}))
-    except Exception:  # threadpoolctl missing: report the affinity set
-        threads, blas = len(os.sched_getaffinity(0)), "unknown"
+    threads, blas = blas_threads()
     lg = T["logits"].cpu().numpy()
     x = moe_inputs.bf16_bits(T["x"])
     w1 = moe_inputs.bf16_bits(T["w1"])
@@ -168,6 +145,197 @@ def cpu_baseline(T, w, forwards, min_seconds=12.0, dropless=False):
                       f"({sum(times):.1f} s in all, median {med:.2f} s), numpy float64 with {blas} BLAS"}
 
 
+def time_graph(torch, step, stream, args):
+    """Capture one step as a hipGraph and time K replays between two HIP
+    events on the launch stream; returns ms per step."""
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            step()
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        warm(graph.replay, args.warmup, args.warmup_seconds, stream)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        ev0.record(stream)
+        for _ in range(args.steps):
+            graph.replay()
+        ev1.record(stream)
+        stream.synchronize()
+        wall = time.perf_counter() - t0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] graph replay: {ms * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
+    return ms
+
+
+def time_calls(torch, names, calls, stream, args):
+    """Average duration of each call's kernels: K eager steps queued back to
+    back with a HIP event between consecutive calls and no host wait between
+    steps, so the host runs ahead and each interval holds the call's kernels,
+    not the host's launch latency."""
+    def step():
+        for c in calls:
+            c()
+    tot = {n: 0.0 for n in names}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(args.steps)]
+    with torch.cuda.stream(stream):
+        warm(step, args.warmup, args.warmup_seconds, stream)
+        for s in range(args.steps):
+            evs[s][0].record(stream)
+            for i, c in enumerate(calls):
+                c()
+                evs[s][i + 1].record(stream)
+        stream.synchronize()
+    for s in range(args.steps):
+        for i, n in enumerate(names):
+            tot[n] += evs[s][i].elapsed_time(evs[s][i + 1])
+    us = {n: tot[n] / args.steps * 1e3 for n in names}
+    log("[bench] eager per-call us: " + ", ".join(f"{n} {us[n]:.1f}" for n in names))
+    return us
+
+
+def roofline(name, flops, nbytes, us, traffic=None):
+    """Roofline of one kernel: its bound is whichever resource needs the
+    longer time at peak; `achieved` is the algorithmic work per launch over
+    the launch time, against that resource's peak."""
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    t_mfma = flops / (PEAK_BF16_TFLOPS * 1e12)
+    gbs = nbytes / (us * 1e-6) / 1e9
+    tflops = flops / (us * 1e-6) / 1e12
+    common = {"kernel": name, "traffic": traffic, "algorithmic_bytes": nbytes, "flops": flops,
+              "launch_us": us, "arithmetic_intensity": flops / nbytes,
+              "attainable_frac": max(t_hbm, t_mfma) / (us * 1e-6)}
+    if t_hbm >= t_mfma:
+        return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": gbs / PEAK_HBM_GBS, "mfma_tflops": tflops,
+                "mfma_frac": tflops / PEAK_BF16_TFLOPS, **common}
+    return {"bound": "mfma", "achieved": tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+            "frac": tflops / PEAK_BF16_TFLOPS, "hbm_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, **common}
+
+
+def backward_work(w, Cp, kept):
+    """Algorithmic work of each call of the training step (forward keeping
+    the pre-activation, then the backward): (flops, bytes) per call."""
+    N, H, I, E, K = w.N, w.H, w.I, w.E, w.K
+    R = E * Cp
+    route = N * E * 4 + N * K * (4 + 4) * 2 + N * K * 4 + E * 4 \
+        + R * 8 + (R // 32) * 4 + E * 4 + N * K * 4 + N * 4 + 4
+    return {
+        "route_capacity_align": (0.0, route),
+        # FC1 + SwiGLU, also writing the 2I pre-activation
+        "fc1_save": (2.0 * R * 2 * I * H, E * 2 * I * H * 2 + N * H * 2 + R * 8 + R * I * 2 + R * 2 * I * 2),
+        "fc2": (2.0 * R * H * I, E * H * I * 2 + R * I * 2 + R * H * 2),
+        "combine": (0.0, kept * H * 2 + N * K * 4 + N * H * 2),
+        # dy gathered (each token row once), W2 streamed, d_act written
+        "fc2_dgrad": (2.0 * R * H * I, E * H * I * 2 + N * H * 2 + R * 4 + R * I * 2),
+        # pre-activation and d_act in; act, d_preact, d_prob out
+        "swiglu_bwd": (0.0, R * 2 * I * 2 + R * I * 2 + R * 4 + R * I * 2 + R * 2 * I * 2 + R * 4),
+        "fc1_dgrad": (2.0 * R * 2 * I * H, E * 2 * I * H * 2 + R * 2 * I * 2 + R * H * 2),
+        "dx_combine": (0.0, kept * H * 2 + N * K * 4 + N * H * 2),
+        # dy rows once, act in, dW2 out
+        "fc2_wgrad": (2.0 * R * H * I, N * H * 2 + R * 4 + R * I * 2 + E * H * I * 2),
+        "fc1_wgrad": (2.0 * R * 2 * I * H, R * 2 * I * 2 + N * H * 2 + R * 4 + E * 2 * I * H * 2),
+        "route_bwd": (0.0, N * K * (4 + 4 + 4 + 4) + N * E * 4),
+    }
+
+
+def bench_backward(args, w, T, torch, moe):
+    """One step = the layer's training step: routing, FC1 keeping the
+    pre-activation, FC2, combine, then the whole backward for a seeded dy."""
+    import moe_inputs
+    buf = moe.MoEBuffers(w.N, w.H, w.I, w.E, w.K, w.F, "cuda")
+    bw = moe.MoEBackwardBuffers(buf)
+    dy = moe_inputs.make_dy(w, "cuda")
+    x, w1, w2 = T["x"], T["w1"], T["w2"]
+    names = ["route_capacity_align", "fc1_save", "fc2", "combine", "fc2_dgrad", "swiglu_bwd",
+             "fc1_dgrad", "dx_combine", "fc2_wgrad", "fc1_wgrad", "route_bwd"]
+    calls = [lambda: buf.route_capacity_align(T["logits"]), lambda: bw.fc1_swiglu_save(x, w1),
+             lambda: buf.fc2(w2), buf.combine, lambda: bw.fc2_dgrad(dy, w2), bw.swiglu_bwd,
+             lambda: bw.fc1_dgrad(w1), bw.dx_combine, lambda: bw.fc2_wgrad(dy),
+             lambda: bw.fc1_wgrad(x), bw.route_bwd]
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+
+    def step():
+        for c in calls:
+            c()
+
+    ms_per_step = time_graph(torch, step, stream, args)
+    us = time_calls(torch, names, calls, stream, args)
+    kept = int((buf.token_routes >= 0).sum().item())
+    work = backward_work(w, buf.Cp, kept)
+    bwd_names = names[4:]
+    dom = max(bwd_names, key=lambda n: us[n])
+    gemms = ["fc1_save", "fc2", "fc2_dgrad", "fc1_dgrad", "fc2_wgrad", "fc1_wgrad"]
+    gflops = sum(work[n][0] for n in gemms)
+    gus = sum(us[n] for n in gemms)
+    rec = {
+        "metric": METRIC.replace("MoE FFN fwd", "MoE FFN fwd+bwd (training step)"),
+        "value": w.N / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + "/fwd+bwd", "N": w.N, "H": w.H, "E": w.E, "K": w.K,
+                   "I": w.I, "F": w.F, "C": buf.C, "Cp": buf.Cp,
+                   "timed": "hipGraph replay of forward (pre-activation kept) + backward"},
+        "gemm_tflops": gflops / (gus * 1e-6) / 1e12,
+        "gemm_frac_bf16_peak": gflops / (gus * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+        "kernel_us": us,
+        "kernel_tflops": {n: work[n][0] / (us[n] * 1e-6) / 1e12 for n in names},
+        "kernel_gbs": {n: work[n][1] / (us[n] * 1e-6) / 1e9 for n in names},
+        "kernel_frac_hbm_peak": {n: work[n][1] / (us[n] * 1e-6) / 1e9 / PEAK_HBM_GBS for n in names},
+        "kept_routes": kept,
+        "roofline": roofline(dom, work[dom][0], work[dom][1], us[dom]),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu_baseline: timing the oracle (forward + backward)")
+        rec["cpu_baseline"] = cpu_baseline_backward(T, dy, w)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+def cpu_baseline_backward(T, dy, w, min_seconds=10.0):
+    import oracle
+    import moe_inputs
+    lg = T["logits"].cpu().numpy()
+    x, w1, w2 = (moe_inputs.bf16_bits(T[k]) for k in ("x", "w1", "w2"))
+    dyb = moe_inputs.bf16_bits(dy)
+    times = []
+    while not times or (sum(times) < min_seconds and len(times) < 5):
+        t0 = time.perf_counter()
+        f = oracle.forward(lg, x, w1, w2, w.K, w.F)
+        oracle.backward(f, x, w1, w2, dyb)
+        times.append(time.perf_counter() - t0)
+        log(f"  oracle forward+backward {len(times)}: {times[-1]:.2f} s")
+    med = statistics.median(times)
+    threads, blas = blas_threads()
+    return {"value": w.N / med, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} full forward+backward passes of the {w.name} workload "
+                      f"({sum(times):.1f} s in all, median {med:.2f} s), numpy float64 with {blas} BLAS"}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        return (max([p.get("num_threads", 1) for p in info] or [1]),
+                ",".join(sorted({p.get("internal_api", "?") for p in info})))
+    except Exception:  # threadpoolctl missing: report the affinity set
+        return len(os.sched_getaffinity(0)), "unknown"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -179,8 +347,9 @@ def main():
     ap.add_argument("--cpu-forwards", type=int, default=3,
                     help="minimum oracle forwards timed for cpu_baseline (more, up to 20, until 12 s of work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", choices=["capacity", "dropless"], default="capacity",
-                    help="fixed-capacity forward (the headline) or the dropless form")
+    ap.add_argument("--variant", choices=["capacity", "dropless", "backward"], default="capacity",
+                    help="fixed-capacity forward (the headline), the dropless form, or the "
+                         "training step (forward keeping the pre-activation + backward)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -203,6 +372,9 @@ def main():
         raise SystemExit("skewed workloads are parity cases, not bench lines")
     log(f"[bench] {w.name}: N={w.N} H={w.H} E={w.E} K={w.K} F={w.F} I={w.I}")
     T = moe_inputs.make_tensors(w, "cuda")
+    if args.variant == "backward":
+        bench_backward(args, w, T, torch, moe)
+        return
     dropless = args.variant == "dropless"
     if dropless:
         buf = moe.DroplessBuffers(w.N, w.H, w.I, w.E, w.K, "cuda")
@@ -215,57 +387,16 @@ def main():
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
 
-    def fwd():
-        route()
-        buf.fc1_swiglu(T["x"], T["w1"])
-        buf.fc2(T["w2"])
-        buf.combine()
-
-    with torch.cuda.stream(stream):
-        for _ in range(3):
-            fwd()
-    stream.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph, stream=stream):
-        fwd()
-    torch.cuda.synchronize()
-
-    # ---- timed region 1: graph replays
-    with torch.cuda.stream(stream):
-        warm(graph.replay, args.warmup, args.warmup_seconds, stream)
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0 = time.perf_counter()
-        ev0.record(stream)
-        for _ in range(args.steps):
-            graph.replay()
-        ev1.record(stream)
-        stream.synchronize()
-        wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] graph replay: {ms_per_step * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
-
-    # ---- timed region 2: eager, one HIP event between consecutive calls
     names = [route_name, "fc1", "fc2", "combine"]
     calls = [route, lambda: buf.fc1_swiglu(T["x"], T["w1"]), lambda: buf.fc2(T["w2"]), buf.combine]
-    # The steps are queued back to back with no host wait between them, so the
-    # host runs ahead and each interval holds the call's kernels, not the
-    # host's launch latency.
-    tot = {n: 0.0 for n in names}
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-           for _ in range(args.steps)]
-    with torch.cuda.stream(stream):
-        warm(fwd, args.warmup, args.warmup_seconds, stream)
-        for s in range(args.steps):
-            evs[s][0].record(stream)
-            for i, c in enumerate(calls):
-                c()
-                evs[s][i + 1].record(stream)
-        stream.synchronize()
-    for s in range(args.steps):
-        for i, n in enumerate(names):
-            tot[n] += evs[s][i].elapsed_time(evs[s][i + 1])
-    us = {n: tot[n] / args.steps * 1e3 for n in names}
-    log("[bench] eager per-call us: " + ", ".join(f"{n} {us[n]:.1f}" for n in names))
+
+    def fwd():
+        for c in calls:
+            c()
+
+    # timed region 1: graph replays; timed region 2: per-call kernel times
+    ms_per_step = time_graph(torch, fwd, stream, args)
+    us = time_calls(torch, names, calls, stream, args)
 
     kept = int((buf.token_routes >= 0).sum().item())
     if dropless:
@@ -305,7 +436,8 @@ def main():
         "kernel_gbs": gbs,
         "kernel_frac_hbm_peak": {n: gbs[n] / PEAK_HBM_GBS for n in names},
         "kept_routes": kept,
-        "roofline": roofline_fc1(fc1_flops, nbytes["fc1"], us["fc1"], traffic),
+        "roofline": roofline("fc1_swiglu (gather-in-GEMM FC1 + SwiGLU*prob)", fc1_flops,
+                             nbytes["fc1"], us["fc1"], traffic),
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the oracle")

@@ -14,13 +14,18 @@
  *
  * The dropless variant ([PF]'s own form: no capacity, every route kept,
  * real extents as device scalars) runs moe_route_dropless,
- * moe_grouped_ffn_fwd_dropless and moe_gather_combine.
+ * moe_grouped_ffn_fwd_dropless and moe_gather_combine;
+ * moe_route_dropless_live in place of the first serves a variable number of
+ * tokens from one static shape.  The backward of the fixed-capacity layer is
+ * declared at the end.
  *
  * Pages defining the operations (cited by title and section):
  *   [FC] "feat(cuda-graphs): capture fixed-capacity MoE execution"
  *        (NVIDIA-NeMo Automodel pull request 2932), Design notes.
  *   [PF] "Permute-Free Grouped GEMM for MoE (bf16, gfx950)"
  *        (ROCm TransformerEngine pull request 694), sections 2-6.
+ *   [BK] "[4/5] feat: capture the FFN experts at bucketed padded shapes"
+ *        (vllm-project afd-plugin pull request 335), What this adds.
  *
  * Conventions shared by every call
  * --------------------------------
@@ -173,6 +178,33 @@ int moe_route_dropless(const float* logits, int64_t N, int32_t E, int32_t K, int
                        int32_t* sorted_slot_ids, float* slot_probs, int32_t* expert_ids,
                        int32_t* block_start, int32_t* token_routes, int32_t* token_route_count,
                        int32_t* num_tokens_post_padded, hipStream_t stream);
+
+/* moe_route_dropless for a variable number of live tokens, read on the
+ * device: [BK] "What this adds" (one shape is captured and every smaller
+ * work item runs in it, its grouping taken from device-side counts).
+ *
+ *   n_live  in  int32 [1]  device scalar, clamped to [0, N]: tokens
+ *                          t < n_live are routed exactly as
+ *                          moe_route_dropless routes the first n_live rows
+ *                          alone; tokens t >= n_live route nowhere
+ *                          (topk_ids -1, topk_probs 0, token_routes -1,
+ *                          token_route_count 0; route_within unspecified) and
+ *                          their logits are not read.
+ *
+ * Every other argument, output and bound is moe_route_dropless's with N the
+ * capacity of the buffers (the static shape a captured graph was built at;
+ * pad slots hold that N as their sentinel row, since rows n_live..N-1 of
+ * the caller's x are real rows with stale contents):
+ * the route list, block map and extent then describe the live tokens only,
+ * so the dropless FFN and the combine do work for them alone and write zero
+ * rows of y for the rest.  A null n_live is MOE_ERR_INVALID_ARG. */
+int moe_route_dropless_live(const float* logits, int64_t N, int32_t E, int32_t K,
+                            const int32_t* n_live, int32_t* topk_ids, float* topk_probs,
+                            int32_t* route_within, int32_t* route_counts,
+                            int32_t* sorted_slot_ids, float* slot_probs, int32_t* expert_ids,
+                            int32_t* block_start, int32_t* token_routes,
+                            int32_t* token_route_count, int32_t* num_tokens_post_padded,
+                            hipStream_t stream);
 
 /* Step 4 over the dropless route list: the same FC1 -> SwiGLU*prob -> FC2
  * as moe_grouped_ffn_fwd, with expert e's rows the slots

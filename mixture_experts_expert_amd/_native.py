@@ -36,6 +36,7 @@ _SIGNATURES = {
     "moe_padded_capacity": (_i64, [_i64]),
     "moe_dropless_bound": (_i64, [_i64, _i32, _i32]),
     "moe_route_dropless": (ctypes.c_int, [_vp, _i64, _i32, _i32] + [_vp] * 12),
+    "moe_route_dropless_live": (ctypes.c_int, [_vp, _i64, _i32, _i32] + [_vp] * 13),
     "moe_grouped_ffn_fwd_dropless": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32,
                                                                 _vp, _vp, _vp]),
     "moe_grouped_fc1_swiglu_dropless": (ctypes.c_int, [_vp] * 6 + [_i64, _i32, _i32, _i32, _i32,
@@ -245,6 +246,28 @@ def moe_route_dropless(logits, K: int, topk_ids, topk_probs, route_within, route
     BM = moe_layout_block_m()
     _check("moe_route_dropless", lib.moe_route_dropless(
         _ptr(logits, torch.float32, N * E, "logits"), N, E, K,
+        _ptr(topk_ids, torch.int32, N * K, "topk_ids"),
+        _ptr(topk_probs, torch.float32, N * K, "topk_probs"),
+        _ptr(route_within, torch.int32, N * K, "route_within"),
+        _ptr(route_counts, torch.int32, E, "route_counts"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"),
+        _ptr(slot_probs, torch.float32, R, "slot_probs"),
+        _ptr(expert_ids, torch.int32, R // BM, "expert_ids"),
+        _ptr(block_start, torch.int32, E, "block_start"),
+        _ptr(token_routes, torch.int32, N * K, "token_routes"),
+        _ptr(token_route_count, torch.int32, N, "token_route_count"),
+        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"), _stream(stream)))
+
+
+def moe_route_dropless_live(logits, K: int, n_live, topk_ids, topk_probs, route_within,
+                            route_counts, sorted_slot_ids, slot_probs, expert_ids, block_start,
+                            token_routes, token_route_count, num_tokens_post_padded, stream=None):
+    N, E = logits.shape
+    R = moe_dropless_bound(N, K, E)
+    BM = moe_layout_block_m()
+    _check("moe_route_dropless_live", lib.moe_route_dropless_live(
+        _ptr(logits, torch.float32, N * E, "logits"), N, E, K,
+        _ptr(n_live, torch.int32, 1, "n_live"),
         _ptr(topk_ids, torch.int32, N * K, "topk_ids"),
         _ptr(topk_probs, torch.float32, N * K, "topk_probs"),
         _ptr(route_within, torch.int32, N * K, "route_within"),

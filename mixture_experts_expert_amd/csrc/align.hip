@@ -79,7 +79,8 @@ __global__ __launch_bounds__(kDlThreads) void align_dropless_kernel(
     const int* __restrict__ route_within, const int* __restrict__ route_counts, int N, int E, int K,
     int R, int* __restrict__ sorted_slot_ids, float* __restrict__ slot_probs,
     int* __restrict__ expert_ids, int* __restrict__ block_start, int* __restrict__ token_routes,
-    int* __restrict__ token_route_count, int* __restrict__ num_tokens_post_padded) {
+    int* __restrict__ token_route_count, int* __restrict__ num_tokens_post_padded,
+    const int* __restrict__ n_live) {
     __shared__ int s_start[kMaxE + 1];   // exclusive prefix of padded counts, s_start[E] = extent
     __shared__ int s_scan[kDlThreads / kWave];
     constexpr int PER = (kMaxE + kDlThreads - 1) / kDlThreads;
@@ -140,7 +141,8 @@ __global__ __launch_bounds__(kDlThreads) void align_dropless_kernel(
             slot_probs[s] = 0.0f;
         }
     }
-    if (i < N) token_route_count[i] = K;
+    // tokens at or past n_live (when given) routed nowhere
+    if (i < N) token_route_count[i] = n_live && i >= min(max(n_live[0], 0), N) ? 0 : K;
     if (i == 0) num_tokens_post_padded[0] = extent;
 }
 
@@ -154,7 +156,7 @@ int launch_align_dropless(const int32_t* topk_ids, const float* topk_probs,
                           int32_t E, int32_t K, int32_t* sorted_slot_ids, float* slot_probs,
                           int32_t* expert_ids, int32_t* block_start, int32_t* token_routes,
                           int32_t* token_route_count, int32_t* num_tokens_post_padded,
-                          hipStream_t stream) {
+                          hipStream_t stream, const int32_t* n_live) {
     const int64_t R = moe_dropless_bound(N, K, E);
     if (R < 0) return static_cast<int>(R);
     const int64_t work = std::max<int64_t>(R, N * K);
@@ -162,7 +164,7 @@ int launch_align_dropless(const int32_t* topk_ids, const float* topk_probs,
     align_dropless_kernel<<<blocks, kDlThreads, 0, stream>>>(
         topk_ids, topk_probs, route_within, route_counts, static_cast<int>(N), E, K,
         static_cast<int>(R), sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
-        token_route_count, num_tokens_post_padded);
+        token_route_count, num_tokens_post_padded, n_live);
     return MOE_OK;
 }
 

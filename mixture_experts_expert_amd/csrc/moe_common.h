@@ -84,6 +84,6 @@ int launch_align_dropless(const int32_t* topk_ids, const float* topk_probs,
                           int32_t E, int32_t K, int32_t* sorted_slot_ids, float* slot_probs,
                           int32_t* expert_ids, int32_t* block_start, int32_t* token_routes,
                           int32_t* token_route_count, int32_t* num_tokens_post_padded,
-                          hipStream_t stream);
+                          hipStream_t stream, const int32_t* n_live = nullptr);
 
 }  // namespace moe

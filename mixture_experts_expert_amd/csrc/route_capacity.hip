@@ -59,11 +59,14 @@ __device__ __forceinline__ void argmax_step(float& bv, int& bi, float ov, int oi
 template <int LPT, int VPL>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, int N, int E, int K, int* __restrict__ topk_ids,
-    float* __restrict__ topk_probs, int* __restrict__ zero_count) {
+    float* __restrict__ topk_probs, int* __restrict__ zero_count, const int* __restrict__ n_live) {
     constexpr int TPB = kTopkThreads / LPT;   // tokens per block
     const int g = threadIdx.x % LPT;          // lane within the token's group
     const int t = blockIdx.x * TPB + threadIdx.x / LPT;
-    const bool live_token = t < N;            // whole groups share t, so exchanges stay in-group
+    // n_live (optional, device data, clamped to [0, N]): tokens at or past it
+    // route nowhere -- expert -1, probability 0 -- and their logits are not read
+    const int nl = n_live ? min(max(n_live[0], 0), N) : N;
+    const bool live_token = t < nl;           // whole groups share t, so exchanges stay in-group
     const float* row = logits + static_cast<size_t>(live_token ? t : 0) * E;
     float v[VPL];
 #pragma unroll
@@ -110,12 +113,12 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
         denom = 0.0;
         for (int k = 0; k < K; ++k) denom += __shfl(ex, k, LPT);
     }
-    if (live_token && g < K) {
-        topk_ids[static_cast<size_t>(t) * K + g] = my_id;
-        topk_probs[static_cast<size_t>(t) * K + g] = static_cast<float>(ex / denom);
+    if (t < N && g < K) {
+        topk_ids[static_cast<size_t>(t) * K + g] = live_token ? my_id : -1;
+        topk_probs[static_cast<size_t>(t) * K + g] = live_token ? static_cast<float>(ex / denom) : 0.0f;
     }
     // the fused align counts kept routes per token with atomics: start at 0
-    if (zero_count && live_token && g == 0) zero_count[t] = 0;
+    if (zero_count && t < N && g == 0) zero_count[t] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -382,27 +385,28 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
 
 template <int LPT, int VPL>
 void launch_topk(const float* logits, int N, int E, int K, int* ids, float* probs, int* zero_count,
-                 hipStream_t s) {
+                 const int* n_live, hipStream_t s) {
     constexpr int TPB = kTopkThreads / LPT;
     const int blocks = (N + TPB - 1) / TPB;
-    route_topk_kernel<LPT, VPL><<<blocks, kTopkThreads, 0, s>>>(logits, N, E, K, ids, probs, zero_count);
+    route_topk_kernel<LPT, VPL><<<blocks, kTopkThreads, 0, s>>>(logits, N, E, K, ids, probs, zero_count,
+                                                                n_live);
 }
 
 // Lanes per token: enough for K (lane k finishes route k) and for E in at
 // most 8 logits per lane when it fits, else all 64 lanes.
 void dispatch_topk(const float* logits, int N, int E, int K, int* ids, float* probs, int* zero_count,
-                   hipStream_t s) {
+                   hipStream_t s, const int* n_live = nullptr) {
     if (K <= 16 && E <= 128) {
-        if (E <= 32) launch_topk<16, 2>(logits, N, E, K, ids, probs, zero_count, s);
-        else if (E <= 64) launch_topk<16, 4>(logits, N, E, K, ids, probs, zero_count, s);
-        else launch_topk<16, 8>(logits, N, E, K, ids, probs, zero_count, s);
+        if (E <= 32) launch_topk<16, 2>(logits, N, E, K, ids, probs, zero_count, n_live, s);
+        else if (E <= 64) launch_topk<16, 4>(logits, N, E, K, ids, probs, zero_count, n_live, s);
+        else launch_topk<16, 8>(logits, N, E, K, ids, probs, zero_count, n_live, s);
     } else if (E <= 256) {
-        if (E <= 128) launch_topk<32, 4>(logits, N, E, K, ids, probs, zero_count, s);
-        else launch_topk<32, 8>(logits, N, E, K, ids, probs, zero_count, s);
+        if (E <= 128) launch_topk<32, 4>(logits, N, E, K, ids, probs, zero_count, n_live, s);
+        else launch_topk<32, 8>(logits, N, E, K, ids, probs, zero_count, n_live, s);
     } else if (E <= 512) {
-        launch_topk<64, 8>(logits, N, E, K, ids, probs, zero_count, s);
+        launch_topk<64, 8>(logits, N, E, K, ids, probs, zero_count, n_live, s);
     } else {
-        launch_topk<64, 16>(logits, N, E, K, ids, probs, zero_count, s);
+        launch_topk<64, 16>(logits, N, E, K, ids, probs, zero_count, n_live, s);
     }
 }
 
@@ -466,13 +470,15 @@ extern "C" int moe_route_capacity_align(const float* logits, int64_t N, int32_t 
     return launch_status();
 }
 
-extern "C" int moe_route_dropless(const float* logits, int64_t N, int32_t E, int32_t K,
-                                  int32_t* topk_ids, float* topk_probs, int32_t* route_within,
-                                  int32_t* route_counts, int32_t* sorted_slot_ids,
-                                  float* slot_probs, int32_t* expert_ids, int32_t* block_start,
-                                  int32_t* token_routes, int32_t* token_route_count,
-                                  int32_t* num_tokens_post_padded, hipStream_t stream) {
-    using namespace moe;
+namespace moe {
+namespace {
+
+int route_dropless(const float* logits, int64_t N, int32_t E, int32_t K, const int32_t* n_live,
+                   int32_t* topk_ids, float* topk_probs, int32_t* route_within,
+                   int32_t* route_counts, int32_t* sorted_slot_ids, float* slot_probs,
+                   int32_t* expert_ids, int32_t* block_start, int32_t* token_routes,
+                   int32_t* token_route_count, int32_t* num_tokens_post_padded,
+                   hipStream_t stream) {
     int st = check_route_shape(N, E, K, N);
     if (st != MOE_OK) return st;
     if (moe_dropless_bound(N, K, E) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
@@ -482,14 +488,44 @@ extern "C" int moe_route_dropless(const float* logits, int64_t N, int32_t E, int
                            token_route_count, num_tokens_post_padded});
     if (st != MOE_OK) return st;
     const int n = static_cast<int>(N);
-    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, nullptr, stream);
+    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, nullptr, stream, n_live);
     // A capacity of N never binds (an expert gets at most one route per
     // token): the selection pass then only ranks each expert's routes in
-    // token order and counts them.
+    // token order and counts them.  Routes of tokens past n_live carry
+    // expert -1 and match no expert.
     capacity_select_kernel<<<E, kSelThreads, 0, stream>>>(topk_ids, topk_probs, n * K, n,
                                                           route_within, route_counts, AlignOut{});
     st = launch_align_dropless(topk_ids, topk_probs, route_within, route_counts, N, E, K,
                                sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
-                               token_route_count, num_tokens_post_padded, stream);
+                               token_route_count, num_tokens_post_padded, stream, n_live);
     return st != MOE_OK ? st : launch_status();
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_route_dropless(const float* logits, int64_t N, int32_t E, int32_t K,
+                                  int32_t* topk_ids, float* topk_probs, int32_t* route_within,
+                                  int32_t* route_counts, int32_t* sorted_slot_ids,
+                                  float* slot_probs, int32_t* expert_ids, int32_t* block_start,
+                                  int32_t* token_routes, int32_t* token_route_count,
+                                  int32_t* num_tokens_post_padded, hipStream_t stream) {
+    return moe::route_dropless(logits, N, E, K, nullptr, topk_ids, topk_probs, route_within,
+                               route_counts, sorted_slot_ids, slot_probs, expert_ids, block_start,
+                               token_routes, token_route_count, num_tokens_post_padded, stream);
+}
+
+extern "C" int moe_route_dropless_live(const float* logits, int64_t N, int32_t E, int32_t K,
+                                       const int32_t* n_live, int32_t* topk_ids,
+                                       float* topk_probs, int32_t* route_within,
+                                       int32_t* route_counts, int32_t* sorted_slot_ids,
+                                       float* slot_probs, int32_t* expert_ids,
+                                       int32_t* block_start, int32_t* token_routes,
+                                       int32_t* token_route_count,
+                                       int32_t* num_tokens_post_padded, hipStream_t stream) {
+    if (!n_live) return MOE_ERR_INVALID_ARG;
+    if (!moe::aligned16(n_live)) return MOE_ERR_MISALIGNED;
+    return moe::route_dropless(logits, N, E, K, n_live, topk_ids, topk_probs, route_within,
+                               route_counts, sorted_slot_ids, slot_probs, expert_ids, block_start,
+                               token_routes, token_route_count, num_tokens_post_padded, stream);
 }

@@ -25,7 +25,8 @@ def test_every_declared_symbol_is_exported():
                           "moe_grouped_ffn_fwd", "moe_grouped_fc1_swiglu", "moe_grouped_fc2",
                           "moe_gather_combine", "moe_grouped_fc1_swiglu_save",
                           "moe_grouped_fc2_dgrad", "moe_swiglu_bwd", "moe_grouped_fc1_dgrad",
-                          "moe_grouped_fc2_wgrad", "moe_grouped_fc1_wgrad", "moe_route_bwd"}
+                          "moe_grouped_fc2_wgrad", "moe_grouped_fc1_wgrad", "moe_route_bwd",
+                          "moe_route_dropless_live"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -108,6 +109,10 @@ def test_dropless_bound_and_validation():
     assert f(ALIGNED, 16, 4, 2, *o[:10], MIS, NUL) == MISALIGNED
     assert f(ALIGNED, 16, 4, 2, *o[:3], NUL, *o[4:], NUL) == INVALID
     assert f(NUL, 0, 4, 2, *([NUL] * 11), NUL) == OK                          # N = 0
+    v = lib.moe_route_dropless_live
+    assert v(ALIGNED, 16, 4, 2, NUL, *o, NUL) == INVALID                      # no live count
+    assert v(ALIGNED, 16, 4, 2, MIS, *o, NUL) == MISALIGNED
+    assert v(ALIGNED, 16, 4, 5, ALIGNED, *o, NUL) == INVALID                  # K > E
     g = lib.moe_grouped_ffn_fwd_dropless
     p7 = [ALIGNED] * 7
     assert g(*p7, 16, 100, 64, 4, 2, ALIGNED, ALIGNED, NUL) == UNSUPPORTED     # H % 64

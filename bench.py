@@ -23,7 +23,9 @@ block-padded segments, the extent a device scalar): its own JSON line, with
 the algorithmic work taken at the real padded extent.  --variant backward
 measures the layer's training step (forward keeping the pre-activation, then
 the backward for a seeded dy), with the roofline of the slowest backward
-kernel.
+kernel.  --variant serving measures variable-N serving of the dropless form
+from a ladder of captured bucket graphs against one graph at the worst-case
+shape and against eager launches (a seeded stream of item sizes).
 """
 
 from __future__ import annotations
@@ -336,6 +338,81 @@ def blas_threads():
         return len(os.sched_getaffinity(0)), "unknown"
 
 
+def bench_serving(args, w, torch, moe):
+    """Variable-N serving of the dropless forward: a seeded stream of items
+    whose token counts cluster just above 0.5x and 1.0x of the expected size
+    (where routing scatter puts them), run three ways on one stream with the
+    inputs resident in HBM: the bucket ladder of captured graphs, one graph
+    at the worst-case shape, and eager launches at each item's exact size."""
+    import numpy as np
+    import moe_inputs
+    expected, top = w.N, 2 * w.N
+    rng = np.random.default_rng(np.random.SeedSequence([w.seed, 7]))
+    items = args.serving_items
+    centers = np.where(rng.random(items) < 0.5, 0.5, 1.0)
+    sizes = np.clip((centers * (1.0 + rng.uniform(0.0, 0.08, items)) * expected).astype(int), 1, top)
+    T = moe_inputs.make_tensors(w, "cuda")
+    lg = torch.from_numpy(moe_inputs.make_logits(top, w.E, w.seed + 100)).to("cuda")
+    g = torch.Generator(device="cuda").manual_seed(w.seed * 1000 + 9)
+    xs = torch.randn(top, w.H, generator=g, device="cuda").to(torch.bfloat16)
+    modes = {
+        "bucketed": moe.ServingLadder(T["w1"], T["w2"], w.K, expected, top, reserve_bytes=8 << 30),
+        "one_graph_at_worst_case": moe.ServingLadder(T["w1"], T["w2"], w.K, expected, top,
+                                                     factors=(2.0,), max_padding_ratio=1e9,
+                                                     reserve_bytes=8 << 30),
+        "eager": moe.ServingLadder(T["w1"], T["w2"], w.K, expected, top, reserve_bytes=1 << 60),
+    }
+    res = {}
+    for name, lad in modes.items():
+        caps = lad.capture()
+        log(f"[bench] serving/{name}: captured buckets {caps}")
+
+        def stream_all():
+            for n in sizes:
+                lad.run(lg[:n], xs[:n])
+        warm(stream_all, 1, args.warmup_seconds, lad.stream)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        ev0.record(lad.stream)
+        for _ in range(args.serving_passes):
+            stream_all()
+        ev1.record(lad.stream)
+        torch.cuda.synchronize()
+        ms = ev0.elapsed_time(ev1) / args.serving_passes
+        res[name] = {"ms_per_pass": ms, "tokens_per_s": float(sizes.sum()) / (ms * 1e-3),
+                     "replays": {str(k): v for k, v in lad.counts.items() if v}}
+        log(f"[bench] serving/{name}: {ms:.2f} ms per pass of {items} items "
+            f"({res[name]['tokens_per_s'] / 1e6:.2f} M tokens/s)")
+        del lad
+        modes[name] = None
+    b = res["bucketed"]
+    rec = {
+        "metric": "routed tokens/s, MoE FFN fwd (dropless), variable-N serving from bucketed hipGraphs, 1 GPU",
+        "value": b["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.serving_passes,
+        "warmup": args.warmup,
+        "ms_per_step": b["ms_per_pass"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name + "/serving", "H": w.H, "E": w.E, "K": w.K, "I": w.I,
+                   "expected_tokens": expected, "max_tokens": top, "items_per_pass": items,
+                   "item_tokens": {"min": int(sizes.min()), "max": int(sizes.max()),
+                                   "mean": float(sizes.mean())},
+                   "timed": "one pass = every item once, inputs resident in HBM"},
+        "modes": res,
+        "bucketed_vs_worst_case_graph": res["one_graph_at_worst_case"]["ms_per_pass"] / b["ms_per_pass"],
+        "bucketed_vs_eager": res["eager"]["ms_per_pass"] / b["ms_per_pass"],
+        "roofline": None,
+        "cpu_baseline": None,
+    }
+    print(json.dumps(rec))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,7 +424,9 @@ def main():
     ap.add_argument("--cpu-forwards", type=int, default=3,
                     help="minimum oracle forwards timed for cpu_baseline (more, up to 20, until 12 s of work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--variant", choices=["capacity", "dropless", "backward"], default="capacity",
+    ap.add_argument("--serving-items", type=int, default=32, help="items per pass (--variant serving)")
+    ap.add_argument("--serving-passes", type=int, default=5, help="timed passes (--variant serving)")
+    ap.add_argument("--variant", choices=["capacity", "dropless", "backward", "serving"], default="capacity",
                     help="fixed-capacity forward (the headline), the dropless form, or the "
                          "training step (forward keeping the pre-activation + backward)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -371,6 +450,9 @@ def main():
     if w.skew:
         raise SystemExit("skewed workloads are parity cases, not bench lines")
     log(f"[bench] {w.name}: N={w.N} H={w.H} E={w.E} K={w.K} F={w.F} I={w.I}")
+    if args.variant == "serving":
+        bench_serving(args, w, torch, moe)
+        return
     T = moe_inputs.make_tensors(w, "cuda")
     if args.variant == "backward":
         bench_backward(args, w, T, torch, moe)

@@ -5,6 +5,8 @@
 // vector-memory waits, and the XCD-aware workgroup renumbering.
 #pragma once
 
+#include <atomic>
+
 #include "moe_common.h"
 
 namespace moe {
@@ -103,6 +105,19 @@ template <int BK>
 __device__ __forceinline__ uint32_t lds_off(int r, int c) {
     constexpr int ROWB = BK * 2, CPR = ROWB / 16, RP = 256 / ROWB;
     return static_cast<uint32_t>(r * ROWB + ((c ^ ((r / RP) % CPR)) << 4));
+}
+
+// Compute units of the current device, queried once per device.
+int device_cus() {
+    static std::atomic<int> cus[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    int n = dev < 64 ? cus[dev].load(std::memory_order_relaxed) : 0;
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 1;
+        if (dev < 64) cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 }  // namespace

@@ -572,19 +572,6 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     wait_vmcnt<0>();   // no DMA may still be writing LDS when the workgroup ends
 }
 
-// Compute units of the current device, queried once per device.
-int device_cus() {
-    static std::atomic<int> cus[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-    int n = dev < 64 ? cus[dev].load(std::memory_order_relaxed) : 0;
-    if (n == 0) {
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 1;
-        if (dev < 64) cus[dev].store(n, std::memory_order_relaxed);
-    }
-    return n;
-}
-
 template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1, bool DYN,
           bool SAVE = false>
 void launch_persistent(const FfnArgs& a, hipStream_t s) {

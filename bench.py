@@ -88,14 +88,15 @@ def algorithmic_bytes_dropless(w, X, Rd, BM):
     }
 
 
-def pmc_traffic(launch_bytes_unit):
+def pmc_traffic(workload):
     """FC1's HBM traffic per launch from the committed rocprofv3 counter summary,
-    scaled by the copy-kernel calibration; None if absent or taken on other code."""
+    scaled by the copy-kernel calibration; None if absent, taken on other code
+    or on another workload."""
     try:
         d = json.load(open(PMC_SUMMARY))
     except (OSError, ValueError):
         return None
-    if d.get("kernel_source_sha") != kernel_source_hash():
+    if d.get("kernel_source_sha") != kernel_source_hash() or d.get("workload") != workload:
         return None
     return int(d["fetch_bytes_per_launch"] * d["fetch_scale"] + d["write_bytes_per_launch"] * d["write_scale"])
 
@@ -489,7 +490,7 @@ def main():
     else:
         rows = w.E * buf.Cp
         nbytes = algorithmic_bytes(w, buf.C, buf.Cp, kept)
-        traffic = pmc_traffic(nbytes["fc1"])
+        traffic = pmc_traffic(w.name)
         shape = {"C": buf.C, "Cp": buf.Cp, "timed": "hipGraph replay of the whole forward"}
     fc1_flops = 2.0 * rows * (2 * w.I) * w.H
     fc2_flops = 2.0 * rows * w.H * w.I

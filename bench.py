@@ -52,9 +52,12 @@ def log(*a):
 
 
 def kernel_source_hash() -> str:
-    """Hash of the FFN kernel source: counter summaries taken on other code are void."""
-    p = os.path.join(ROOT, "mixture_experts_expert_amd", "csrc", "grouped_ffn.hip")
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+    """Hash of the FFN kernel's sources (the kernel file and the headers it
+    includes): counter summaries taken on other code are void."""
+    h = hashlib.sha256()
+    for f in ("grouped_ffn.hip", "gemm_common.h", "moe_common.h"):
+        h.update(open(os.path.join(ROOT, "mixture_experts_expert_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def algorithmic_bytes(w, C, Cp, kept):

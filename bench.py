@@ -104,6 +104,26 @@ def pmc_traffic(workload):
     return int(d["fetch_bytes_per_launch"] * d["fetch_scale"] + d["write_bytes_per_launch"] * d["write_scale"])
 
 
+def copy_rate(torch, stream, nbytes=1 << 30, reps=10):
+    """GB/s of a plain device-to-device copy (read + write bytes), the HBM
+    headroom the kernels are compared against."""
+    src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda")
+    dst = torch.empty_like(src)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            dst.copy_(src)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(reps):
+            dst.copy_(src)
+        ev1.record(stream)
+        stream.synchronize()
+    gbs = 2 * nbytes * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
+    log(f"[bench] device copy: {gbs:.0f} GB/s")
+    return gbs
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling the FETCH/WRITE counters."""
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
@@ -151,9 +171,11 @@ def cpu_baseline(T, w, forwards, min_seconds=12.0, dropless=False):
                       f"({sum(times):.1f} s in all, median {med:.2f} s), numpy float64 with {blas} BLAS"}
 
 
-def time_graph(torch, step, stream, args):
+def time_graph(torch, step, stream, args, stats=None):
     """Capture one step as a hipGraph and time K replays between two HIP
-    events on the launch stream; returns ms per step."""
+    events on the launch stream; returns ms per step.  With `stats` (a dict),
+    K more replays are timed one by one (an event pair around each) and their
+    median and 90th percentile go into it, in microseconds."""
     with torch.cuda.stream(stream):
         for _ in range(3):
             step()
@@ -174,6 +196,18 @@ def time_graph(torch, step, stream, args):
         wall = time.perf_counter() - t0
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] graph replay: {ms * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
+    if stats is not None:
+        with torch.cuda.stream(stream):
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            evs[0].record(stream)
+            for i in range(args.steps):
+                graph.replay()
+                evs[i + 1].record(stream)
+            stream.synchronize()
+        each = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps))
+        stats["median"] = statistics.median(each)
+        stats["p90"] = each[min(len(each) - 1, int(0.9 * len(each)))]
+        log(f"[bench] single replays: median {stats['median']:.1f} us, p90 {stats['p90']:.1f} us")
     return ms
 
 
@@ -481,7 +515,8 @@ def main():
             c()
 
     # timed region 1: graph replays; timed region 2: per-call kernel times
-    ms_per_step = time_graph(torch, fwd, stream, args)
+    replay = {}
+    ms_per_step = time_graph(torch, fwd, stream, args, replay)
     us = time_calls(torch, names, calls, stream, args)
 
     kept = int((buf.token_routes >= 0).sum().item())
@@ -516,11 +551,20 @@ def main():
         "config": {"workload": w.name + ("/dropless" if dropless else ""), "N": w.N, "H": w.H,
                    "E": w.E, "K": w.K, "I": w.I, **({} if dropless else {"F": w.F}), **shape},
         "routes_per_s": w.N * w.K / (ms_per_step * 1e-3),
+        "replay_us": replay,
         "gemm_tflops": gemm_tflops,
         "gemm_frac_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+        # the same GEMM time credited only with the kept routes' work
+        "useful_tflops": 6.0 * w.H * w.I * kept / ((us["fc1"] + us["fc2"]) * 1e-6) / 1e12,
         "kernel_us": us,
         "kernel_gbs": gbs,
         "kernel_frac_hbm_peak": {n: gbs[n] / PEAK_HBM_GBS for n in names},
+        # the scan / scatter / gather steps together (routing call + combine)
+        "route_combine_frac_hbm_peak": (nbytes[route_name] + nbytes["combine"])
+                                       / ((us[route_name] + us["combine"]) * 1e-6) / 1e9 / PEAK_HBM_GBS,
+        # torch's own device copy: a reference point for HBM rates, not a
+        # ceiling (the combine kernel runs above it)
+        "torch_copy_gbs": copy_rate(torch, stream),
         "kept_routes": kept,
         "roofline": roofline("fc1_swiglu (gather-in-GEMM FC1 + SwiGLU*prob)", fc1_flops,
                              nbytes["fc1"], us["fc1"], traffic),

@@ -94,3 +94,35 @@ def check_combine_stepwise(buf: MoEBuffers, N):
     y = oracle.gather_combine(host(buf.route_out), host(buf.token_routes), N)
     g = host(buf.y)
     assert np.array_equal(g, y), f"combine differs in {(g != y).sum()} elements"
+
+
+# Backward bars (the derivation is in test_gpu_backward's module notes):
+# elementwise |gpu - ref| <= ATOL_RMS * rms(ref) + RTOL * |ref| (+ 2^-7 times
+# the summed magnitudes of separately rounded terms, end to end) and a
+# normwise relative error <= NORM_TOL; float32 results step-wise at F32_TOL.
+ATOL_RMS = 1e-2
+F32_TOL = 1e-3
+
+
+def grad_vals(v):
+    v = np.asarray(v)
+    return oracle.bf16_bits_to_f64(v) if v.dtype == np.uint16 else v.astype(np.float64)
+
+
+def assert_grad_close(gpu, ref, what, rtol=RTOL, atol_rms=ATOL_RMS, norm_tol=NORM_TOL, terms=None):
+    """terms: for a result that sums separately rounded bf16 values, the
+    elementwise sum of their magnitudes; one ulp (2^-8 relative) may flip in
+    each of them, so 2^-7 * terms joins the bar."""
+    g, r = grad_vals(gpu), grad_vals(ref)
+    assert g.shape == r.shape, (what, g.shape, r.shape)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    d = np.abs(g - r)
+    bar = atol_rms * rms + rtol * np.abs(r)
+    if terms is not None:
+        bar = bar + 2.0 ** -7 * terms
+    bad = d > bar
+    nr = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
+    say(f"  {what}: normwise rel err {nr:.2e}, max abs err {d.max(initial=0):.2e} "
+        f"(rms {rms:.2e}), exact {float(np.mean(g == r)) if g.size else 1.0:.4f}")
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements outside the bar"
+    assert nr <= norm_tol, f"{what}: normwise relative error {nr:.3e}"

@@ -34,40 +34,13 @@ import torch
 
 import moe_inputs
 import oracle
-from gpu_support import check_capacity_and_align, check_routing, host, say
+from gpu_support import (F32_TOL, assert_grad_close, check_capacity_and_align, check_routing, grad_vals,
+                         host, say)
 from mixture_experts_expert_amd import MoEBackwardBuffers, MoEBuffers
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-RTOL, ATOL_RMS, NORM_TOL = 2e-2, 1e-2, 1e-2
-F32_TOL = 1e-3
-
-
-def _vals(v):
-    v = np.asarray(v)
-    return oracle.bf16_bits_to_f64(v) if v.dtype == np.uint16 else v.astype(np.float64)
-
-
-def assert_grad_close(gpu, ref, what, rtol=RTOL, atol_rms=ATOL_RMS, norm_tol=NORM_TOL, terms=None):
-    """terms: for a result that sums separately rounded bf16 values, the
-    elementwise sum of their magnitudes; one ulp (2^-8 relative) may flip in
-    each of them, so 2^-7 * terms joins the bar."""
-    g, r = _vals(gpu), _vals(ref)
-    assert g.shape == r.shape, (what, g.shape, r.shape)
-    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
-    d = np.abs(g - r)
-    bar = atol_rms * rms + rtol * np.abs(r)
-    if terms is not None:
-        bar = bar + 2.0 ** -7 * terms
-    bad = d > bar
-    nr = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
-    say(f"  {what}: normwise rel err {nr:.2e}, max abs err {d.max(initial=0):.2e} "
-        f"(rms {rms:.2e}), exact {float(np.mean(g == r)) if g.size else 1.0:.4f}")
-    assert not bad.any(), f"{what}: {int(bad.sum())} elements outside the bar"
-    assert nr <= norm_tol, f"{what}: normwise relative error {nr:.3e}"
-
-
 def run_case(N, H, I, E, K, F, T, dy):
     buf = MoEBuffers(N, H, I, E, K, F, DEV)
     bw = MoEBackwardBuffers(buf)
@@ -128,14 +101,14 @@ def check_backward(s, T, dy):
     # Each end-to-end result sums separately rounded bf16 values; its bar
     # adds 2^-7 times the sum of those terms' magnitudes (see above).
     tr = m["token_routes"]
-    da_abs = np.abs(_vals(R["d_a"]))
+    da_abs = np.abs(grad_vals(R["d_a"]))
     dx_terms = np.zeros((N, H))
     for k in range(K):
         sel = tr[:, k] >= 0
         dx_terms[sel] += da_abs[tr[sel, k]]
     assert_grad_close(g_dx, R["dx"], "dx (end to end)", terms=dx_terms)
-    xa, dya = np.abs(_vals(x)), np.abs(_vals(dyb))
-    dpa, aca = np.abs(_vals(R["d_preact"])), np.abs(_vals(R["act"]))
+    xa, dya = np.abs(grad_vals(x)), np.abs(grad_vals(dyb))
+    dpa, aca = np.abs(grad_vals(R["d_preact"])), np.abs(grad_vals(R["act"]))
 
     def rows(src, e):
         r = ssi[e * Cp:(e + 1) * Cp]
@@ -149,9 +122,9 @@ def check_backward(s, T, dy):
     assert_grad_close(host(bw.dw2), R["dw2"], "dw2 (end to end)", terms=dw2_terms)
     # d_logits = p_k (dp_k - sum_j p_j dp_j), dp a sum over the I columns of
     # d_act * silu(g) * u with d_act and the pre-activation rounded upstream
-    pre = _vals(R["preact"])
+    pre = grad_vals(R["preact"])
     g_, u_ = pre[:, :I], pre[:, I:]
-    dp_terms = (np.abs(_vals(R["d_act"])) * np.abs(g_ / (1 + np.exp(-g_)) * u_)).sum(axis=1)
+    dp_terms = (np.abs(grad_vals(R["d_act"])) * np.abs(g_ / (1 + np.exp(-g_)) * u_)).sum(axis=1)
     pk = host(buf.topk_probs).astype(np.float64)
     ak = np.where(tr >= 0, dp_terms[np.maximum(tr, 0)], 0.0)
     gk = pk * (ak + (pk * ak).sum(axis=1, keepdims=True))

@@ -11,8 +11,12 @@
 //   by the shapes alone.
 //
 // gfx950 design (not the pages' FlyDSL kernel):
-//   * one workgroup per (expert, M-tile, N-tile); the M-tile spans up to 256
-//     slots so an expert's weight panel is streamed from HBM once;
+//   * 256x256 tiles over (expert, M-tile, N-tile); the M-tile spans an
+//     expert's whole capacity (up to 256 slots, 320 in the dropless form) so
+//     its weight panel is streamed from HBM once;
+//   * persistent workgroups (one per resident slot) walk the tiles, and the
+//     LDS load rings run across tile boundaries: the last K steps of a tile
+//     already fetch the first slabs of the workgroup's next tile;
 //   * bf16 MFMA 32x32x16 with float32 accumulators;
 //   * operands are K-contiguous on both sides (x rows, weight rows), staged
 //     through LDS in 64-wide K slabs with an XOR swizzle of the 16-byte

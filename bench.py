@@ -26,6 +26,8 @@ the backward for a seeded dy), with the roofline of the slowest backward
 kernel.  --variant serving measures variable-N serving of the dropless form
 from a ladder of captured bucket graphs against one graph at the worst-case
 shape and against eager launches (a seeded stream of item sizes).
+--variant ep-local measures the grouped FFN on one expert-parallel rank's
+share (--ep, default 8): E/ep experts with C*ep received rows each.
 """
 
 from __future__ import annotations
@@ -346,6 +348,92 @@ def bench_backward(args, w, T, torch, moe):
     print(json.dumps(rec))
 
 
+def bench_ep_local(args, w, torch, moe):
+    """One step = the grouped FFN (FC1 + SwiGLU, FC2) on one expert-parallel
+    rank's share of the layer: E/ep local experts with C*ep received rows
+    each, already grouped by expert (the route list is the identity).  The
+    exchange itself needs more than one GPU and is not timed."""
+    import moe_inputs
+    ep = args.ep
+    C = int(moe.moe_source_capacity(w.N, w.K, w.E, w.F)) * ep
+    d = moe_inputs.make_ep_local(w, ep, C, "cuda")
+    E = d["E"]
+    N = E * C
+    H, I = w.H, w.I
+    ssi = torch.arange(N, dtype=torch.int32, device="cuda")
+    act = torch.empty(N, I, dtype=torch.bfloat16, device="cuda")
+    ro = torch.empty(N, H, dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    names = ["fc1", "fc2"]
+    calls = [lambda: moe.moe_grouped_fc1_swiglu(d["x"], d["w1"], ssi, d["probs"], C, act, stream),
+             lambda: moe.moe_grouped_fc2(act, d["w2"], N, C, ro, stream)]
+
+    def step():
+        for c in calls:
+            c()
+
+    ms_per_step = time_graph(torch, step, stream, args)
+    us = time_calls(torch, names, calls, stream, args)
+    flops = {"fc1": 2.0 * N * 2 * I * H, "fc2": 2.0 * N * H * I}
+    nbytes = {"fc1": E * 2 * I * H * 2 + N * H * 2 + N * 8 + N * I * 2,
+              "fc2": E * H * I * 2 + N * I * 2 + N * H * 2}
+    gemm_tflops = (flops["fc1"] + flops["fc2"]) / ((us["fc1"] + us["fc2"]) * 1e-6) / 1e12
+    rec = {
+        "metric": f"expert-parallel rank's grouped FFN (EP={ep} share): rows/s + grouped-GEMM TFLOP/s "
+                  "(% bf16 MFMA peak), 1 GPU",
+        "value": N / (ms_per_step * 1e-3),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}/ep{ep}-local", "E_local": E, "rows_per_expert": C,
+                   "rows": N, "H": H, "I": I,
+                   "timed": "hipGraph replay of FC1 + FC2 on the rank's received rows"},
+        "gemm_tflops": gemm_tflops,
+        "gemm_frac_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
+        "kernel_us": us,
+        "kernel_tflops": {n: flops[n] / (us[n] * 1e-6) / 1e12 for n in names},
+        "kernel_gbs": {n: nbytes[n] / (us[n] * 1e-6) / 1e9 for n in names},
+        "roofline": roofline("fc1_swiglu (FC1 + SwiGLU*prob on the received rows)", flops["fc1"],
+                             nbytes["fc1"], us["fc1"]),
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] cpu_baseline: timing the oracle on one local expert")
+        rec["cpu_baseline"] = cpu_baseline_ep_local(d, E, C)
+    else:
+        rec["cpu_baseline"] = None
+    print(json.dumps(rec))
+
+
+def cpu_baseline_ep_local(d, E, C, min_seconds=10.0):
+    """The oracle's expert FFN on the rows of one local expert (repeated for
+    at least ``min_seconds``), scaled to the rank's E experts."""
+    import moe_inputs
+    import oracle
+    threads, blas = blas_threads()
+    x = moe_inputs.bf16_bits(d["x"][:C])
+    w1 = moe_inputs.bf16_bits(d["w1"][0])
+    w2 = moe_inputs.bf16_bits(d["w2"][0])
+    p = d["probs"][:C].cpu().numpy()
+    times = []
+    while len(times) < 2 or sum(times) < min_seconds:
+        t0 = time.perf_counter()
+        oracle.expert_ffn(x, w1, w2, p)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": C / med, "unit": "rows/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{len(times)} runs of oracle.expert_ffn on one local expert's {C} rows "
+                      f"({sum(times):.1f} s in all, median {med:.2f} s; the rank's step is {E} such experts), "
+                      f"numpy float64 with {blas} BLAS"}
+
+
 def cpu_baseline_backward(T, dy, w, min_seconds=10.0):
     import oracle
     import moe_inputs
@@ -464,7 +552,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--serving-items", type=int, default=32, help="items per pass (--variant serving)")
     ap.add_argument("--serving-passes", type=int, default=5, help="timed passes (--variant serving)")
-    ap.add_argument("--variant", choices=["capacity", "dropless", "backward", "serving"], default="capacity",
+    ap.add_argument("--ep", type=int, default=8, help="expert-parallel degree (--variant ep-local)")
+    ap.add_argument("--variant", choices=["capacity", "dropless", "backward", "serving", "ep-local"],
+                    default="capacity",
                     help="fixed-capacity forward (the headline), the dropless form, or the "
                          "training step (forward keeping the pre-activation + backward)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -490,6 +580,9 @@ def main():
     log(f"[bench] {w.name}: N={w.N} H={w.H} E={w.E} K={w.K} F={w.F} I={w.I}")
     if args.variant == "serving":
         bench_serving(args, w, torch, moe)
+        return
+    if args.variant == "ep-local":
+        bench_ep_local(args, w, torch, moe)
         return
     T = moe_inputs.make_tensors(w, "cuda")
     if args.variant == "backward":

@@ -40,6 +40,9 @@
  *   the supported envelope fails closed (no fallback path):
  *       1 <= K <= min(E, 32),  1 <= E <= 1024,  0 <= N <= 16384,
  *       H and I multiples of 64 in [64, 16384],
+ *       (the grouped FFN calls of step 4 take any N their 32-bit offsets
+ *       allow, (N + 1) * H * 2 < 2^31: after an expert-parallel exchange a
+ *       rank's received rows exceed the routing envelope),
  *       C = the value moe_source_capacity returns for (N, K, E, F).
  *   N == 0 is a no-op that returns MOE_OK.
  * - After launching, the call maps hipGetLastError() != hipSuccess to

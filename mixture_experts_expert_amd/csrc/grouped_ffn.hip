@@ -671,7 +671,10 @@ int check_ffn(int64_t N, int32_t H, int32_t I, int32_t E, int64_t C, int* Cp) {
     if (N < 0 || E < 1 || C < 0) return MOE_ERR_INVALID_ARG;
     int st = check_dims(H, I);
     if (st != MOE_OK) return st;
-    if (N > kMaxN || E > kMaxE) return MOE_ERR_UNSUPPORTED;
+    // N is bounded only by the 32-bit offsets below: the GEMMs take any row
+    // count (an expert-parallel rank's received rows exceed the routing
+    // envelope), unlike the routing calls
+    if (N > INT32_MAX || E > kMaxE) return MOE_ERR_UNSUPPORTED;
     const int64_t Cp64 = moe_padded_capacity(C);
     if (Cp64 < 0) return MOE_ERR_UNSUPPORTED;
     const int64_t big = static_cast<int64_t>(1) << 31;

@@ -140,6 +140,32 @@ def make_dy(w: Workload, device="cpu") -> torch.Tensor:
     return _normal_bf16((w.N, w.H), 1.0, g, device)
 
 
+def make_ep_local(w: Workload, ep: int, rows_per_expert: int, device="cpu") -> dict:
+    """What one rank's expert FFN holds after an expert-parallel exchange of
+    workload ``w`` at degree ``ep``: E/ep local experts, each with
+    ``rows_per_expert`` rows (the caller's capacity times ep), already grouped
+    by expert -- x bf16 [E/ep * rows, H] ~ N(0, 1), w1 bf16 [E/ep, 2I, H] and
+    w2 bf16 [E/ep, H, I] ~ N(0, 0.02), and the rows' routing probabilities
+    float32 [E/ep * rows] ~ U(0, 1).  Torch's generator on ``device``, seeded
+    with seed*1000 + 10 + {1, 2, 3, 4}."""
+    if ep < 1 or w.E % ep or rows_per_expert < 1:
+        raise ValueError(f"ep must divide E = {w.E}; rows_per_expert must be positive")
+    device = torch.device(device)
+    El = w.E // ep
+    rows = rows_per_expert
+    g = torch.Generator(device=device)
+    out = {"E": El, "C": rows}
+    g.manual_seed(w.seed * 1000 + 11)
+    out["x"] = _normal_bf16((El * rows, w.H), 1.0, g, device)
+    g.manual_seed(w.seed * 1000 + 12)
+    out["w1"] = _normal_bf16((El, 2 * w.I, w.H), 0.02, g, device)
+    g.manual_seed(w.seed * 1000 + 13)
+    out["w2"] = _normal_bf16((El, w.H, w.I), 0.02, g, device)
+    g.manual_seed(w.seed * 1000 + 14)
+    out["probs"] = torch.rand(El * rows, generator=g, device=device, dtype=torch.float32)
+    return out
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Host uint16 view of a bf16 tensor's bit patterns."""
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)

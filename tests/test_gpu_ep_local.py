@@ -1,0 +1,69 @@
+"""The grouped FFN on one expert-parallel rank's share: after the exchange a
+rank holds E/ep experts with C*ep rows each, already grouped by expert, so
+the route list is the identity (slot s reads row s) and the row count
+exceeds the routing calls' envelope (N = E*C rows: 32768 at the
+Qwen3-30B-A3B shape for any ep).  The GEMMs take any row count their 32-bit
+offsets allow.
+
+* a small layer with N > 16384 rows, every slot checked against the oracle;
+* the Qwen3-30B-A3B shape at ep = 8 (16 local experts, 2048 rows each, the
+  configuration `bench.py --variant ep-local` times): two experts checked in
+  full and four sampled rows of every other expert.
+
+Bars: the forward's (act and route_out within 1e-2 + 2e-2|ref| and normwise
+1e-2), oracle.expert_ffn / oracle.grouped_ffn on the same rows.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import oracle
+from gpu_support import assert_bf16_close, host, say
+from mixture_experts_expert_amd import moe_grouped_fc1_swiglu, moe_grouped_fc2
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(d, stream=None):
+    E, C = d["E"], d["C"]
+    N = E * C
+    ssi = torch.arange(N, dtype=torch.int32, device="cuda")
+    act = torch.full((N, d["w2"].shape[2]), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ro = torch.full((N, d["w2"].shape[1]), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    moe_grouped_fc1_swiglu(d["x"], d["w1"], ssi, d["probs"], C, act, stream)
+    moe_grouped_fc2(act, d["w2"], N, C, ro, stream)
+    torch.cuda.synchronize()
+    return ssi, act, ro
+
+
+def test_more_rows_than_the_routing_envelope():
+    w = moe_inputs.Workload("ep_local_small", 64, 128, 8, 2, 1.0, 64, 21)
+    d = moe_inputs.make_ep_local(w, 2, 4608, "cuda")        # 4 experts x 4608 rows = 18432
+    ssi, act, ro = _run(d)
+    N = d["E"] * d["C"]
+    assert N > 16384
+    r_act, r_ro = oracle.grouped_ffn(host(d["x"]), host(d["w1"]), host(d["w2"]), host(ssi),
+                                     host(d["probs"]), d["E"], d["C"])
+    assert_bf16_close(host(act), r_act, "act")
+    assert_bf16_close(host(ro), r_ro, "route_out")
+
+
+def test_qwen_shape_ep8_share():
+    w = moe_inputs.WORKLOADS["qwen3_30b_a3b_n4096_h2048_e128_k8"]
+    ep = 8
+    C = oracle.source_capacity(w.N, w.K, w.E, w.F) * ep
+    d = moe_inputs.make_ep_local(w, ep, C, "cuda")
+    _, act, ro = _run(d)
+    E = d["E"]
+    say(f"  {E} local experts x {C} rows = {E * C} rows")
+    x, pr = host(d["x"]), host(d["probs"])
+    rng = np.random.default_rng(3)
+    full = set(rng.choice(E, size=2, replace=False).tolist())
+    for e in range(E):
+        rows = np.arange(e * C, (e + 1) * C) if e in full else np.sort(rng.choice(np.arange(e * C, (e + 1) * C), 4, replace=False))
+        r_act, r_out = oracle.expert_ffn(x[rows], host(d["w1"][e]), host(d["w2"][e]), pr[rows])
+        idx = torch.as_tensor(rows, device="cuda")
+        assert_bf16_close(host(act[idx]), r_act, f"act e{e}")
+        assert_bf16_close(host(ro[idx]), r_out, f"route_out e{e}")

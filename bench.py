@@ -106,6 +106,32 @@ def pmc_traffic(workload):
     return int(d["fetch_bytes_per_launch"] * d["fetch_scale"] + d["write_bytes_per_launch"] * d["write_scale"])
 
 
+def vendor_reference(torch, moe, w, args):
+    """torch's bf16 batched matmul (hipBLASLt) on the layer's per-expert
+    products, E x (Cp x 2I x H) and E x (Cp x H x I), without the gather and
+    the epilogue: one JSON line of microseconds and TFLOP/s."""
+    Cp = int(moe.moe_padded_capacity(moe.moe_source_capacity(w.N, w.K, w.E, w.F)))
+    out = {"workload": w.name, "kind": "torch bf16 bmm (hipBLASLt), per-expert products"}
+    stream = torch.cuda.Stream()
+    for name, (M, N, K) in (("fc1", (Cp, 2 * w.I, w.H)), ("fc2", (Cp, w.H, w.I))):
+        g = torch.Generator(device="cuda").manual_seed(7)
+        a = torch.randn(w.E, M, K, generator=g, device="cuda").to(torch.bfloat16)
+        b = torch.randn(w.E, K, N, generator=g, device="cuda").to(torch.bfloat16).contiguous()
+        with torch.cuda.stream(stream):
+            warm(lambda: torch.bmm(a, b), args.warmup, args.warmup_seconds, stream)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(args.steps):
+                torch.bmm(a, b)
+            ev1.record(stream)
+            stream.synchronize()
+        us = ev0.elapsed_time(ev1) / args.steps * 1e3
+        out[name] = {"shape": [w.E, M, N, K], "us": us, "tflops": 2.0 * w.E * M * N * K / us / 1e6}
+        log(f"[bench] vendor bmm {name} {w.E}x({M}x{N}x{K}): {us:.1f} us, {out[name]['tflops']:.0f} TFLOP/s")
+        del a, b
+    print(json.dumps(out))
+
+
 def copy_rate(torch, stream, nbytes=1 << 30, reps=10):
     """GB/s of a plain device-to-device copy (read + write bytes), the HBM
     headroom the kernels are compared against."""
@@ -557,6 +583,9 @@ def main():
                     default="capacity",
                     help="fixed-capacity forward (the headline), the dropless form, or the "
                          "training step (forward keeping the pre-activation + backward)")
+    ap.add_argument("--vendor-reference", action="store_true",
+                    help="only time torch's bf16 batched GEMM (hipBLASLt) at the layer's per-expert "
+                         "FC1 and FC2 shapes, as context for the grouped kernels, and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
     args = ap.parse_args()
@@ -575,6 +604,9 @@ def main():
         return
 
     w = moe_inputs.WORKLOADS[args.workload or moe_inputs.HEADLINE]
+    if args.vendor_reference:
+        vendor_reference(torch, moe, w, args)
+        return
     if w.skew:
         raise SystemExit("skewed workloads are parity cases, not bench lines")
     log(f"[bench] {w.name}: N={w.N} H={w.H} E={w.E} K={w.K} F={w.F} I={w.I}")

@@ -107,6 +107,37 @@ __device__ __forceinline__ uint32_t lds_off(int r, int c) {
     return static_cast<uint32_t>(r * ROWB + ((c ^ ((r / RP) % CPR)) << 4));
 }
 
+typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// K-major LDS stages (one K row per LDS row, 16-byte chunks swizzled
+// chunk ^ 4*(row%4)) feed the MFMA through gfx950's ds_read_b64_tr_b16,
+// which hands lane i of a 16-lane group element i%4 of the 8-byte pieces
+// addressed by lanes 4j + i/4 (j = 0..3): with lane c addressing row
+// k0 + c/4, columns n0 + 4(c%4) .. +3, lane i receives column n0 + i of rows
+// k0 .. k0+3.  Two such reads give a lane its 8 consecutive K values.
+//
+// Byte offset, within a K-major stage (rows of ROWB bytes), of the 8-byte
+// piece that lane `lane` addresses in a transpose read of the 32-wide column
+// block at column t, K rows kb .. kb+7 (read r = 0 or 1 covers kb+4r ..).
+template <int ROWB>
+__device__ __forceinline__ uint32_t tr_off(int lane, int t, int kb, int r) {
+    const int g = lane >> 4, i = lane & 15;
+    const int col = t + 16 * (g & 1) + 4 * (i & 3);
+    const int k = kb + 8 * (g >> 1) + 4 * r + (i >> 2);
+    const int lc = col >> 3, half = (col >> 2) & 1;
+    return static_cast<uint32_t>(k * ROWB + ((lc ^ (4 * (k & 3))) << 4) + half * 8);
+}
+
+__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* stage, uint32_t off0, uint32_t off1) {
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off0));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off1));
+    typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
+    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 // Compute units of the current device, queried once per device.
 int device_cus() {
     static std::atomic<int> cus[64];

@@ -43,11 +43,10 @@
 #include <initializer_list>
 
 #include "gemm_common.h"
+#include "slot_gemm.h"
 
 namespace moe {
 namespace {
-
-typedef short i16x4 __attribute__((__vector_size__(4 * sizeof(short))));
 
 enum RowSrc : int {
     kRowWeight = 0,   // row k of expert e's weight matrix
@@ -71,31 +70,8 @@ struct BwdArgs {
 
 typedef const __attribute__((address_space(4))) int* const_int_ptr;
 
-// Byte offset, within a K-major stage (rows of ROWB bytes), of the 8-byte
-// piece that lane `lane` addresses in a transpose read of the 32-wide column
-// block at column t, K rows kb .. kb+7 (read r = 0 or 1 covers kb+4r ..).
-template <int ROWB>
-__device__ __forceinline__ uint32_t tr_off(int lane, int t, int kb, int r) {
-    const int g = lane >> 4, i = lane & 15;
-    const int col = t + 16 * (g & 1) + 4 * (i & 3);
-    const int k = kb + 8 * (g >> 1) + 4 * r + (i >> 2);
-    const int lc = col >> 3, half = (col >> 2) & 1;
-    return static_cast<uint32_t>(k * ROWB + ((lc ^ (4 * (k & 3))) << 4) + half * 8);
-}
-
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
 // cache-policy operand of a buffer store: non-temporal (streamed)
 constexpr int kStoreNT = 2;
-
-__device__ __forceinline__ bf16x8 tr_frag(const lds_u8* stage, uint32_t off0, uint32_t off1) {
-    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off0));
-    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off1));
-    typedef short i16x8 __attribute__((__vector_size__(8 * sizeof(short))));
-    const i16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-    return __builtin_bit_cast(bf16x8, v);
-}
 
 // Data gradient: out rows are the expert's slots, A is row-major by slot
 // (the expert's segment of a route-ordered buffer, or gathered token rows),
@@ -531,6 +507,26 @@ int launch_dgrad(BwdArgs a, int E, hipStream_t s) {
     return MOE_OK;
 }
 
+// FC1 dgrad (A = the route-ordered d_preact) runs on the producer/consumer
+// slot GEMM: the same tiles and K order as dgrad_kernel, the same results bit
+// for bit, ≈ 5% faster (the FC2 dgrad, whose gathered dy rows would need
+// per-tile token loads in the producers, stays on dgrad_kernel).
+int launch_fc1_dgrad(const BwdArgs& a, int E, hipStream_t s) {
+    SlotArgs sa{};
+    sa.a = a.a; sa.b = a.b; sa.out = a.out;
+    sa.lda = a.lda; sa.ldb = a.ldb; sa.ldo = a.ldo;
+    sa.N = a.N; sa.Nn = a.Nn; sa.Kd = a.Kd; sa.Cp = a.Cp;
+    sa.MT = (a.Cp + 255) / 256;
+    sa.NT = (a.Nn + 255) / 256;
+    const int64_t tiles = static_cast<int64_t>(E) * sa.MT * sa.NT;
+    if (tiles > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    sa.tiles = static_cast<int>(tiles);
+    sa.b_estride = a.b_estride;
+    sa.krot = 0;
+    slot_gemm_kernel<kSlotRoute, true><<<std::min(sa.tiles, device_cus()), 12 * kWave, 0, s>>>(sa);
+    return MOE_OK;
+}
+
 template <int ASRC, int BSRC>
 int launch_wgrad(BwdArgs a, int E, hipStream_t s) {
     constexpr int BT = 256;                        // square output tiles
@@ -607,7 +603,7 @@ extern "C" int moe_grouped_fc1_dgrad(const uint16_t* d_preact, const uint16_t* w
     a.lda = 2 * I; a.ldb = H; a.ldo = H; a.N = static_cast<int>(N);
     a.M = Cp; a.Nn = H; a.Kd = 2 * I; a.Cp = Cp;
     a.b_estride = static_cast<int64_t>(2) * I * H;
-    st = launch_dgrad<kRowRoute>(a, E, stream);
+    st = launch_fc1_dgrad(a, E, stream);
     return st != MOE_OK ? st : launch_status();
 }
 

@@ -35,6 +35,7 @@
 #include <initializer_list>
 
 #include "gemm_common.h"
+#include "slot_gemm.h"
 
 namespace moe {
 namespace {
@@ -647,7 +648,28 @@ int pick_tile_dyn(double mean) {
 
 // Fixed segments tile Cp; variable ones (dyn) take their shape from the mean
 // number of routes per expert, which only steers performance.
+// FC2 over whole 256-row tiles runs on the producer/consumer slot GEMM: its
+// loading waves never wait on the route_out stores (same tiles, same K
+// order, the same results bit for bit as the one-role kernel, a few percent
+// faster).
+int launch_fc2_slots(const FfnArgs& a, int E, hipStream_t s) {
+    SlotArgs sa{};
+    sa.a = a.a; sa.b = a.w; sa.out = a.out;
+    sa.lda = a.Kdim; sa.ldb = a.Kdim; sa.ldo = a.ncols;
+    sa.N = a.N; sa.Nn = a.ncols; sa.Kd = a.Kdim; sa.Cp = a.Cp;
+    sa.MT = (a.Cp + 255) / 256;
+    sa.NT = (a.ncols + 255) / 256;
+    const int64_t tiles = static_cast<int64_t>(E) * sa.MT * sa.NT;
+    if (tiles > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    sa.tiles = static_cast<int>(tiles);
+    sa.b_estride = static_cast<int64_t>(a.wrows) * a.Kdim;
+    sa.krot = kKRotate;
+    slot_gemm_kernel<kSlotRoute, false><<<std::min(sa.tiles, device_cus()), 12 * kWave, 0, s>>>(sa);
+    return MOE_OK;
+}
+
 int launch(const FfnArgs& a, bool fc1, int E, hipStream_t s, bool dyn = false, double mean = 0.0) {
+    if (!fc1 && !dyn && a.Kdim >= 128 && pick_tile_m(a.Cp) == 256) return launch_fc2_slots(a, E, s);
     if (a.Kdim < 128) {
         // a 64-long contraction: 32-wide K slabs, so a tile has the two
         // steps the cross-tile look-ahead needs

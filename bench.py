@@ -57,7 +57,7 @@ def kernel_source_hash() -> str:
     """Hash of the FFN kernel's sources (the kernel file and the headers it
     includes): counter summaries taken on other code are void."""
     h = hashlib.sha256()
-    for f in ("grouped_ffn.hip", "gemm_common.h", "moe_common.h"):
+    for f in ("grouped_ffn.hip", "slot_gemm.h", "gemm_common.h", "moe_common.h"):
         h.update(open(os.path.join(ROOT, "mixture_experts_expert_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

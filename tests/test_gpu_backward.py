@@ -176,6 +176,11 @@ EDGE = {
     "overload_one_expert": (Shape(512, 64, 128, 8, 2, 1.0), "hot"),
     "large_factor_pads": (Shape(200, 64, 128, 8, 2, 4.0), None),
     "wide_e1000_k32": (Shape(256, 64, 64, 1000, 32, 1.0), None),
+    # C = 256 and 512: whole 256-row tiles (the persistent 12-wave GEMM), one
+    # with ragged column tiles (H = 320, I = 192) and a 3-slab contraction, one
+    # with two row tiles per expert
+    "whole_tiles_ragged_h320_i192": (Shape(512, 320, 192, 8, 4, 1.0), None),
+    "two_row_tiles_c512": (Shape(1024, 256, 128, 8, 4, 1.0), None),
 }
 
 

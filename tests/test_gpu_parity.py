@@ -97,6 +97,11 @@ EDGE = {
     "e100_k7_f2": (Shape(1000, 128, 64, 100, 7, 2.0), None),
     "large_factor_pads": (Shape(200, 64, 128, 8, 2, 4.0), None),
     "max_tokens_all_to_one": (Shape(16384, 64, 64, 64, 6, 1.0), "hot"),
+    # C = 256 and 512: whole 256-row tiles (the persistent 12-wave GEMM), one
+    # with ragged column tiles (H = 320, I = 192) and a 3-slab contraction, one
+    # with two row tiles per expert
+    "whole_tiles_ragged_h320_i192": (Shape(512, 320, 192, 8, 4, 1.0), None),
+    "two_row_tiles_c512": (Shape(1024, 256, 128, 8, 4, 1.0), None),
 }
 
 

@@ -37,6 +37,7 @@ import hashlib
 import json
 import os
 import statistics
+import subprocess
 import sys
 import time
 
@@ -60,6 +61,33 @@ def kernel_source_hash() -> str:
     for f in ("grouped_ffn.hip", "slot_gemm.h", "gemm_common.h", "moe_common.h"):
         h.update(open(os.path.join(ROOT, "mixture_experts_expert_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
+
+
+def provenance(torch) -> dict:
+    """What produced the numbers: a hash of every library source, the commit
+    when the tree is a git checkout, and the ROCm / torch / device it ran on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "mixture_experts_expert_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(csrc, f), "rb").read())
+    h.update(open(os.path.join(ROOT, "include", "moe_native.h"), "rb").read())
+    git = None
+    if os.path.isdir(os.path.join(ROOT, ".git")):
+        try:
+            git = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                                 text=True, timeout=10).stdout.strip() or None
+        except (OSError, subprocess.SubprocessError):
+            git = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        rocm = None
+    props = torch.cuda.get_device_properties(0)
+    return {"source_sha": h.hexdigest()[:16], "git_sha": git, "rocm": rocm, "hip": torch.version.hip,
+            "torch": torch.__version__, "device": props.name,
+            "arch": getattr(props, "gcnArchName", None)}
 
 
 def algorithmic_bytes(w, C, Cp, kept):
@@ -354,6 +382,7 @@ def bench_backward(args, w, T, torch, moe):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "env": provenance(torch),
         "config": {"workload": w.name + "/fwd+bwd", "N": w.N, "H": w.H, "E": w.E, "K": w.K,
                    "I": w.I, "F": w.F, "C": buf.C, "Cp": buf.Cp,
                    "timed": "hipGraph replay of forward (pre-activation kept) + backward"},
@@ -419,6 +448,7 @@ def bench_ep_local(args, w, torch, moe):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "env": provenance(torch),
         "config": {"workload": f"{w.name}/ep{ep}-local", "E_local": E, "rows_per_expert": C,
                    "rows": N, "H": H, "I": I,
                    "timed": "hipGraph replay of FC1 + FC2 on the rank's received rows"},
@@ -551,6 +581,7 @@ def bench_serving(args, w, torch, moe):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "env": provenance(torch),
         "config": {"workload": w.name + "/serving", "H": w.H, "E": w.E, "K": w.K, "I": w.I,
                    "expected_tokens": expected, "max_tokens": top, "items_per_pass": items,
                    "item_tokens": {"min": int(sizes.min()), "max": int(sizes.max()),
@@ -673,6 +704,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
+        "env": provenance(torch),
         "config": {"workload": w.name + ("/dropless" if dropless else ""), "N": w.N, "H": w.H,
                    "E": w.E, "K": w.K, "I": w.I, **({} if dropless else {"F": w.F}), **shape},
         "routes_per_s": w.N * w.K / (ms_per_step * 1e-3),

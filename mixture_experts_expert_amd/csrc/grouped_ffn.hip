@@ -656,7 +656,7 @@ int launch_fc2_slots(const FfnArgs& a, int E, hipStream_t s) {
     SlotArgs sa{};
     sa.a = a.a; sa.b = a.w; sa.out = a.out;
     sa.lda = a.Kdim; sa.ldb = a.Kdim; sa.ldo = a.ncols;
-    sa.N = a.N; sa.Nn = a.ncols; sa.Kd = a.Kdim; sa.Cp = a.Cp;
+    sa.Nn = a.ncols; sa.Kd = a.Kdim; sa.Cp = a.Cp;
     sa.MT = (a.Cp + 255) / 256;
     sa.NT = (a.ncols + 255) / 256;
     const int64_t tiles = static_cast<int64_t>(E) * sa.MT * sa.NT;
@@ -664,7 +664,7 @@ int launch_fc2_slots(const FfnArgs& a, int E, hipStream_t s) {
     sa.tiles = static_cast<int>(tiles);
     sa.b_estride = static_cast<int64_t>(a.wrows) * a.Kdim;
     sa.krot = kKRotate;
-    slot_gemm_kernel<kSlotRoute, false><<<std::min(sa.tiles, device_cus()), 12 * kWave, 0, s>>>(sa);
+    slot_gemm_kernel<false><<<std::min(sa.tiles, device_cus()), 12 * kWave, 0, s>>>(sa);
     return MOE_OK;
 }
 

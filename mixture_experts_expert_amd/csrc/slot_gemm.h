@@ -1,16 +1,14 @@
 // Grouped GEMM whose output rows are an expert's slots (internal):
 //
-//   out[seg + s, n] = sum_k A[row(s), k] * B_e[k, n]     s < Cp, n < Nn, k < Kd
+//   out[seg + s, n] = sum_k A[seg + s, k] * B_e[k, n]     s < Cp, n < Nn, k < Kd
 //
-// with row(s) the slot itself (A route-ordered) or the token the route list
-// names (A token-ordered, gathered; the sentinel N reads as a zero row), and
-// B_e expert e's weight matrix, stored N-major ([Nn][Kd], FC2's W2 in the
-// forward) or K-major ([Kd][Nn], the transposed-weight view of a dgrad).
+// with A route-ordered (row s of expert e's segment seg = e*Cp) and B_e expert
+// e's weight matrix, stored N-major ([Nn][Kd], FC2's W2 in the forward) or
+// K-major ([Kd][Nn], the transposed-weight view of a dgrad).
 //
 // [PF] "Permute-Free Grouped GEMM for MoE (bf16, gfx950)", sections 3 and 5:
 // FC2 of the forward (A = act by route position) and the FC1 data gradient
-// (A = d_preact by route position, B = W1 read K-major); gathered A rows are
-// supported too.
+// (A = d_preact by route position, B = W1 read K-major).
 //
 // gfx950 design: bf16 MFMA 32x32x16 with float32 accumulators, 256x256 output
 // tiles, 64-deep K slabs staged through LDS by DMA rings (A two stages deep,
@@ -28,18 +26,11 @@
 namespace moe {
 namespace {
 
-enum SlotRows : int {
-    kSlotRoute = 1,    // A row s of the expert's segment of a route-ordered buffer
-    kSlotGather = 2,   // A row sorted_slot_ids[s] of a token-ordered buffer
-};
-
 struct SlotArgs {
     const uint16_t* a;            // A rows (row-major, K contiguous)
     const uint16_t* b;            // expert weights, b_estride elements apart
-    const int* sorted_slot_ids;   // gathered A only
     uint16_t* out;                // [E*Cp, ldo]
     int lda, ldb, ldo;            // row pitches in elements
-    int N;                        // token rows of a gathered A
     int Nn, Kd;                   // output columns, contraction length
     int Cp;                       // slots per expert
     int MT, NT, tiles;            // tiles per expert (M, N), all tiles
@@ -47,7 +38,7 @@ struct SlotArgs {
     int krot;                     // expert e starts its K walk at slab (e*krot) % KT
 };
 
-template <int ASRC, bool BKM>
+template <bool BKM>
 __global__ __launch_bounds__(768) void slot_gemm_kernel(SlotArgs p) {
     constexpr int BMT = 256, BNT = 256, BK = 64, WM = 2, WN = 4, NA = 2, NB = 3;
     constexpr int NC = WM * WN;                    // consumer waves
@@ -99,27 +90,11 @@ __global__ __launch_bounds__(768) void slot_gemm_kernel(SlotArgs p) {
             const int seg = min(e, p.tiles / (p.MT * p.NT) - 1) * p.Cp;   // pointers past the end read nothing
             const bool live = d.t < p.tiles;
             d.rot = (e * p.krot) % KT;
-            d.r = ASRC == kSlotGather ? make_rsrc(p.a, static_cast<uint32_t>(p.N) * a_rowb)
-                                      : make_rsrc(p.a + static_cast<int64_t>(seg) * p.lda,
-                                                  static_cast<uint32_t>(len) * a_rowb);
+            d.r = make_rsrc(p.a + static_cast<int64_t>(seg) * p.lda, static_cast<uint32_t>(len) * a_rowb);
 #pragma unroll
             for (int i = 0; i < A_INST; ++i) {
-                const int blk = A_RPI * (pw + i * NP);            // first tile row of the load (uniform)
-                const int r = blk + lane / A_CPR;
-                int row = -1;
-                if (ASRC == kSlotGather) {
-                    if (live && m0 + blk < len) {
-                        // the load's A_RPI slots, through the scalar cache
-                        typedef const __attribute__((address_space(4))) int* cip;
-                        const cip q = (cip)(p.sorted_slot_ids) + seg + m0 + blk;
-                        int tok = q[0];
-#pragma unroll
-                        for (int j = 1; j < A_RPI; ++j) { const int v = q[j]; tok = lane / A_CPR == j ? v : tok; }
-                        row = static_cast<unsigned>(tok) < static_cast<unsigned>(p.N) ? tok : -1;
-                    }
-                } else {
-                    row = live && m0 + r < len ? m0 + r : -1;
-                }
+                const int r = A_RPI * (pw + i * NP) + lane / A_CPR;   // tile row
+                const int row = live && m0 + r < len ? m0 + r : -1;
                 const int chunk = (lane % A_CPR) ^ ((r / (256 / AROWB)) % A_CPR);
                 d.base[i] = row < 0 ? kOob : static_cast<uint32_t>(row) * a_rowb + chunk * 16u;
             }

@@ -34,9 +34,11 @@
 //   * K-major stages swizzle their 16-byte chunks by row (chunk ^ 4*(row%4)):
 //     the four rows of one transpose read then fall on disjoint banks;
 //   * gathered rows come straight from token order through the route list;
-//   * dgrad: one workgroup of 8 waves per output tile (long K: the loads
+//   * FC2 dgrad: one workgroup of 8 waves per output tile (long K: the loads
 //     overlap the MFMAs within the tile); consecutive tiles (same expert,
 //     neighbouring N-tiles) are renumbered onto the same XCD;
+//   * FC1 dgrad: the persistent producer/consumer slot GEMM (slot_gemm.h),
+//     whose consumer waves store without waiting on the loads;
 //   * wgrad: short K and a large output per tile, so one persistent
 //     workgroup per CU with producer and consumer waves (below).
 #include <algorithm>

@@ -28,7 +28,10 @@
 //     routing probability are applied to the accumulators in registers and
 //     only the I-wide bf16 activation is written;
 //   * tiles are renumbered so that consecutive tiles (same expert, adjacent
-//     N-tiles, sharing the gathered A rows) land on the same XCD and its L2.
+//     N-tiles, sharing the gathered A rows) land on the same XCD and its L2;
+//   * FC2 over whole 256-row tiles runs on the producer/consumer slot GEMM
+//     (slot_gemm.h): waves that only load and waves that only compute and
+//     store, so the route_out stores never hold up a load wait.
 #include <algorithm>
 #include <atomic>
 #include <cmath>

@@ -434,6 +434,21 @@ def bench_ep_local(args, w, torch, moe):
     nbytes = {"fc1": E * 2 * I * H * 2 + N * H * 2 + N * 8 + N * I * 2,
               "fc2": E * H * I * 2 + N * I * 2 + N * H * 2}
     gemm_tflops = (flops["fc1"] + flops["fc2"]) / ((us["fc1"] + us["fc2"]) * 1e-6) / 1e12
+    # the dispatch side on a source rank: route the whole layer's tokens, then
+    # pack the send buffer (each slot's token row in route order)
+    T = moe_inputs.make_tensors(w, "cuda", weights=False)
+    src = moe.MoEBuffers(w.N, H, I, w.E, w.K, w.F, "cuda")
+    src.route_capacity_align(T["logits"])
+    R = src.sorted_slot_ids.shape[0]
+    send = torch.empty(R, H, dtype=torch.bfloat16, device="cuda")
+    torch.cuda.synchronize()
+    kept = int((src.token_routes >= 0).sum().item())
+    pack_us = time_calls(torch, ["dispatch_rows"],
+                         [lambda: moe.moe_dispatch_rows(T["x"], src.sorted_slot_ids, send, stream)],
+                         stream, args)["dispatch_rows"]
+    pack_bytes = kept * H * 2 + R * 4 + R * H * 2
+    log(f"[bench] dispatch rows (source rank, {R} slot rows): {pack_us:.1f} us, "
+        f"{pack_bytes / (pack_us * 1e-6) / 1e9:.0f} GB/s")
     rec = {
         "metric": f"expert-parallel rank's grouped FFN (EP={ep} share): rows/s + grouped-GEMM TFLOP/s "
                   "(% bf16 MFMA peak), 1 GPU",
@@ -459,6 +474,11 @@ def bench_ep_local(args, w, torch, moe):
         "kernel_gbs": {n: nbytes[n] / (us[n] * 1e-6) / 1e9 for n in names},
         "roofline": roofline("fc1_swiglu (FC1 + SwiGLU*prob on the received rows)", flops["fc1"],
                              nbytes["fc1"], us["fc1"]),
+        # not part of the timed step: the source rank's send-buffer pack
+        # before the exchange (moe_dispatch_rows), eager, HIP events
+        "dispatch_rows": {"us": pack_us, "slot_rows": R, "algorithmic_bytes": pack_bytes,
+                          "gbs": pack_bytes / (pack_us * 1e-6) / 1e9,
+                          "frac_hbm_peak": pack_bytes / (pack_us * 1e-6) / 1e9 / PEAK_HBM_GBS},
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the oracle on one local expert")

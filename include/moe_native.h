@@ -279,6 +279,27 @@ int moe_grouped_fc2(const uint16_t* act, const uint16_t* w2, int64_t N, int32_t 
 int moe_gather_combine(const uint16_t* route_out, const int32_t* token_routes, int64_t N,
                        int32_t K, int32_t H, int64_t R, uint16_t* y, hipStream_t stream);
 
+/* Dispatch rows for an expert-parallel exchange: the send buffer of a
+ * uniform all-to-all, each slot's token row in route order,
+ *   rows[s] = x[sorted_slot_ids[s]]   (a zero row where the entry is not a
+ *                                      token index in [0, N): the pads)
+ * [FC] Design notes: with a fixed capacity every source rank sends exactly
+ * C rows per expert, so expert e's segment [e*Cp, (e+1)*Cp) goes whole to
+ * the rank that owns e; [PF] section 4: pad slots name the sentinel row N,
+ * which carries zeros.  Received rows are already grouped by expert, so a
+ * rank runs the grouped FFN on them with the identity route list
+ * (sorted_slot_ids[s] = s), and route_out comes back in this same order for
+ * moe_gather_combine.  On one GPU this is the whole dispatch side of that
+ * exchange except the transfer itself.
+ *
+ *   x                in  bf16  [N, H] (token order)
+ *   sorted_slot_ids  in  int32 [R]    (R = E*Cp; entries range-checked)
+ *   rows             out bf16  [R, H], every row written
+ * N may exceed the routing envelope (up to INT32_MAX); H a multiple of 64 up
+ * to 16384.  R == 0 returns MOE_OK without launching. */
+int moe_dispatch_rows(const uint16_t* x, const int32_t* sorted_slot_ids, int64_t N, int32_t H,
+                      int64_t R, uint16_t* rows, hipStream_t stream);
+
 /* ------------------------------------------------------------------------
  * Backward (training) of the fixed-capacity layer
  *

@@ -12,6 +12,7 @@ from ._native import (  # noqa: F401
     header_functions,
     lib,
     moe_align,
+    moe_dispatch_rows,
     moe_dropless_bound,
     moe_gather_combine,
     moe_grouped_fc1_dgrad,

@@ -54,6 +54,7 @@ _SIGNATURES = {
                                               _vp, _vp]),
     "moe_grouped_fc2": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _vp]),
     "moe_gather_combine": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i64, _vp, _vp]),
+    "moe_dispatch_rows": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i64, _vp, _vp]),
     "moe_grouped_fc1_swiglu_save": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                                    _i64, _vp, _vp, _vp]),
     "moe_grouped_fc2_dgrad": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp,
@@ -236,6 +237,14 @@ def moe_gather_combine(route_out, token_routes, y, stream=None):
         _ptr(route_out, torch.bfloat16, R * H, "route_out"),
         _ptr(token_routes, torch.int32, N * K, "token_routes"), N, K, H, R,
         _ptr(y, torch.bfloat16, N * H, "y"), _stream(stream)))
+
+
+def moe_dispatch_rows(x, sorted_slot_ids, rows, stream=None):
+    N, H = x.shape
+    R = sorted_slot_ids.shape[0]
+    _check("moe_dispatch_rows", lib.moe_dispatch_rows(
+        _ptr(x, torch.bfloat16, N * H, "x"), _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"),
+        N, H, R, _ptr(rows, torch.bfloat16, R * H, "rows"), _stream(stream)))
 
 
 def moe_route_dropless(logits, K: int, topk_ids, topk_probs, route_within, route_counts,

@@ -55,6 +55,26 @@ __global__ __launch_bounds__(256) void gather_combine_kernel(
     *reinterpret_cast<uint4*>(y + static_cast<int64_t>(t) * H + c * 8) = o;
 }
 
+// Dispatch side of an expert-parallel exchange: the send buffer holds each
+// slot's token row in route order, rows[s] = x[sorted_slot_ids[s]], with a
+// zero row for the sentinel (pads) -- the rows a uniform all-to-all moves,
+// C per expert from every source.  Work item = one 16-byte chunk of one
+// slot row; HBM-bound (the kept rows read, every slot row written once).
+__global__ __launch_bounds__(256) void dispatch_rows_kernel(
+    const uint16_t* __restrict__ x, const int* __restrict__ sorted_slot_ids, int N, int H, int R,
+    uint16_t* __restrict__ rows) {
+    const int chunks = H / 8;
+    const int64_t item = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (item >= static_cast<int64_t>(R) * chunks) return;
+    const int s = static_cast<int>(item / chunks);
+    const int c = static_cast<int>(item - static_cast<int64_t>(s) * chunks);
+    const int tok = sorted_slot_ids[s];
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (static_cast<unsigned>(tok) < static_cast<unsigned>(N))   // device data: range-checked
+        v = *reinterpret_cast<const uint4*>(x + static_cast<int64_t>(tok) * H + c * 8);
+    *reinterpret_cast<uint4*>(rows + static_cast<int64_t>(s) * H + c * 8) = v;
+}
+
 template <int KMAX>
 void launch_combine(const uint16_t* ro, const int* tr, int N, int K, int H, int R, uint16_t* y,
                     hipStream_t s) {
@@ -80,5 +100,21 @@ extern "C" int moe_gather_combine(const uint16_t* route_out, const int32_t* toke
     else if (K <= 8) launch_combine<8>(route_out, token_routes, n, K, H, r, y, stream);
     else if (K <= 16) launch_combine<16>(route_out, token_routes, n, K, H, r, y, stream);
     else launch_combine<32>(route_out, token_routes, n, K, H, r, y, stream);
+    return launch_status();
+}
+
+extern "C" int moe_dispatch_rows(const uint16_t* x, const int32_t* sorted_slot_ids, int64_t N,
+                                 int32_t H, int64_t R, uint16_t* rows, hipStream_t stream) {
+    using namespace moe;
+    if (N < 0 || H < 1 || R < 0) return MOE_ERR_INVALID_ARG;
+    if (N > INT32_MAX || H % 64 || H > kMaxDim || R > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (R == 0) return MOE_OK;
+    if (!x || !sorted_slot_ids || !rows) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(sorted_slot_ids) || !aligned16(rows)) return MOE_ERR_MISALIGNED;
+    const int64_t items = R * (H / 8);
+    const int64_t blocks = (items + 255) / 256;
+    if (blocks > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    dispatch_rows_kernel<<<static_cast<int>(blocks), 256, 0, stream>>>(
+        x, sorted_slot_ids, static_cast<int>(N), H, static_cast<int>(R), rows);
     return launch_status();
 }

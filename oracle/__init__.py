@@ -37,6 +37,7 @@ from .moe import (  # noqa: F401
     grouped_ffn,
     grouped_ffn_blocks,
     padded_capacity,
+    dispatch_rows,
     permuted_forward,
     route_topk,
     source_capacity,

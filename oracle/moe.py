@@ -20,6 +20,8 @@ capacity_select       per-expert keep-by-probability         brute force, domina
 align                 block-padded route list + inverse map  hand-worked example, invariants
 grouped_ffn           gather FC1 -> SwiGLU*prob -> FC2        library SwiGLU (E=1,K=1), dense path
 gather_combine        per-token sum of its kept routes       dense path, hand-worked example
+dispatch_rows         route-ordered copy of the token rows   inverse of the route list,
+                      (a permute; an EP send buffer)         permuted = permute-free FFN
 permuted_forward      materialised-permute formulation       cross-check only
 dense_forward         per-token formulation, no capacity     cross-check only
 dropless_bound        static route-list bound, dropless      closed form
@@ -309,6 +311,23 @@ def forward(logits, x_bits, w1_bits, w2_bits, K: int, F: float, BM: int = BM_DEF
     return out
 
 
+def dispatch_rows(x_bits, sorted_slot_ids):
+    """Route-ordered copy of the token rows: row s is x[sorted_slot_ids[s]],
+    a zero row where the entry is not a token index (the sentinel N of a pad).
+
+    [PF] section 1 calls this the materialised permute; [FC] Design notes:
+    with a fixed capacity it is also the send buffer of a uniform
+    expert-parallel exchange, C rows per expert from every source.
+    """
+    x_bits = np.asarray(x_bits, dtype=np.uint16)
+    N, H = x_bits.shape
+    ssi = np.asarray(sorted_slot_ids, dtype=np.int64)
+    rows = np.zeros((ssi.shape[0], H), dtype=np.uint16)
+    real = (ssi >= 0) & (ssi < N)
+    rows[real] = x_bits[ssi[real]]
+    return rows
+
+
 def permuted_forward(x_bits, w1_bits, w2_bits, meta, E: int):
     """[PF] section 1: the conventional path with a materialised permute.
 
@@ -321,8 +340,7 @@ def permuted_forward(x_bits, w1_bits, w2_bits, meta, E: int):
     N, H = x_bits.shape
     Cp = meta["Cp"]
     ssi = meta["sorted_slot_ids"]
-    xp = np.zeros((E * Cp, H), dtype=np.uint16)
-    xp[ssi < N] = x_bits[ssi[ssi < N]]
+    xp = dispatch_rows(x_bits, ssi)
     blocks = []
     for e in range(E):
         seg = slice(e * Cp, (e + 1) * Cp)

@@ -26,7 +26,7 @@ def test_every_declared_symbol_is_exported():
                           "moe_gather_combine", "moe_grouped_fc1_swiglu_save",
                           "moe_grouped_fc2_dgrad", "moe_swiglu_bwd", "moe_grouped_fc1_dgrad",
                           "moe_grouped_fc2_wgrad", "moe_grouped_fc1_wgrad", "moe_route_bwd",
-                          "moe_route_dropless_live"}
+                          "moe_route_dropless_live", "moe_dispatch_rows"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -158,6 +158,18 @@ def test_combine_validation():
     assert f(ALIGNED, ALIGNED, 16, 2, 72, 128, ALIGNED, NUL) == UNSUPPORTED
     assert f(ALIGNED, MIS, 16, 2, 64, 128, ALIGNED, NUL) == MISALIGNED
     assert f(NUL, NUL, 0, 2, 64, 0, NUL, NUL) == OK
+
+
+def test_dispatch_rows_validation():
+    f = lib.moe_dispatch_rows
+    assert f(ALIGNED, ALIGNED, -1, 64, 128, ALIGNED, NUL) == INVALID
+    assert f(ALIGNED, ALIGNED, 16, 0, 128, ALIGNED, NUL) == INVALID
+    assert f(ALIGNED, ALIGNED, 16, 64, -1, ALIGNED, NUL) == INVALID
+    assert f(ALIGNED, ALIGNED, 16, 72, 128, ALIGNED, NUL) == UNSUPPORTED
+    assert f(ALIGNED, ALIGNED, 16, 64, 2**31, ALIGNED, NUL) == UNSUPPORTED
+    assert f(NUL, ALIGNED, 16, 64, 128, ALIGNED, NUL) == INVALID
+    assert f(ALIGNED, MIS, 16, 64, 128, ALIGNED, NUL) == MISALIGNED
+    assert f(NUL, NUL, 16, 64, 0, NUL, NUL) == OK          # no slots: nothing to write
 
 
 def test_backward_validation():

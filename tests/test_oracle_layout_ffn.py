@@ -145,6 +145,42 @@ def test_permuted_equals_permute_free_bitwise():
     assert np.array_equal(yp, o["y"])
 
 
+def test_dispatch_rows_invert_the_route_list():
+    """The route-ordered copy holds, for every kept route (t, k), token t's
+    row at the slot the inverse map names; pads are zero rows; each token's
+    row appears once per kept route and nowhere else."""
+    w, lg, x, w1, w2 = _tiny_inputs()
+    o = oracle.forward(lg, x, w1, w2, w.K, 1.5)
+    rows = oracle.dispatch_rows(x, o["sorted_slot_ids"])
+    assert rows.shape == (w.E * o["Cp"], w.H)
+    tr = o["token_routes"]
+    filled = np.zeros(rows.shape[0], bool)
+    for t in range(w.N):
+        for k in range(w.K):
+            s = tr[t, k]
+            if s >= 0:
+                assert np.array_equal(rows[s], x[t])
+                filled[s] = True
+    assert filled.sum() == (tr >= 0).sum()                   # one slot per kept route
+    pads = ~filled
+    assert pads.sum() > 0 and np.all(rows[pads] == 0)
+    # a token row with a nonzero value is found exactly where its routes went
+    assert np.array_equal(np.flatnonzero(filled), np.flatnonzero(o["sorted_slot_ids"] < w.N))
+
+
+def test_ffn_on_dispatched_rows_equals_permute_free():
+    """An expert-parallel rank runs the grouped FFN on received rows with
+    the identity route list; on the dispatched copy that must equal the
+    permute-free FFN over the original route list, bit for bit."""
+    w, lg, x, w1, w2 = _tiny_inputs()
+    o = oracle.forward(lg, x, w1, w2, w.K, w.F)
+    rows = oracle.dispatch_rows(x, o["sorted_slot_ids"])
+    R = rows.shape[0]
+    act, ro = oracle.grouped_ffn(rows, w1, w2, np.arange(R), o["slot_probs"], w.E, o["Cp"])
+    assert np.array_equal(act, o["act"]) and np.array_equal(ro, o["route_out"])
+    assert np.array_equal(oracle.gather_combine(ro, o["token_routes"], w.N), o["y"])
+
+
 def test_dense_formulation_no_drops():
     """With C >= every expert's load nothing drops, and the slot machinery
     must reproduce the per-token sum of p * FFN_e(x)."""

@@ -430,6 +430,16 @@ def bench_ep_local(args, w, torch, moe):
 
     ms_per_step = time_graph(torch, step, stream, args)
     us = time_calls(torch, names, calls, stream, args)
+    # the receive buffer as an all-to-all leaves it (source-major): FC1 reads
+    # it in expert order through a fixed route list
+    perm = torch.as_tensor(moe_inputs.ep_receive_order(E, ep, C // ep), device="cuda")
+    x_recv = torch.empty_like(d["x"])
+    x_recv[perm.long()] = d["x"]
+    act_sm = torch.empty_like(act)
+    torch.cuda.synchronize()
+    us_sm = time_calls(torch, ["fc1_source_major"],
+                       [lambda: moe.moe_grouped_fc1_swiglu(x_recv, d["w1"], perm, d["probs"], C, act_sm,
+                                                           stream)], stream, args)["fc1_source_major"]
     flops = {"fc1": 2.0 * N * 2 * I * H, "fc2": 2.0 * N * H * I}
     nbytes = {"fc1": E * 2 * I * H * 2 + N * H * 2 + N * 8 + N * I * 2,
               "fc2": E * H * I * 2 + N * I * 2 + N * H * 2}
@@ -474,6 +484,8 @@ def bench_ep_local(args, w, torch, moe):
         "kernel_gbs": {n: nbytes[n] / (us[n] * 1e-6) / 1e9 for n in names},
         "roofline": roofline("fc1_swiglu (FC1 + SwiGLU*prob on the received rows)", flops["fc1"],
                              nbytes["fc1"], us["fc1"]),
+        # FC1 on the source-major receive buffer through its route list
+        "fc1_source_major_us": us_sm,
         # not part of the timed step: the source rank's send-buffer pack
         # before the exchange (moe_dispatch_rows), eager, HIP events
         "dispatch_rows": {"us": pack_us, "slot_rows": R, "algorithmic_bytes": pack_bytes,

@@ -166,6 +166,17 @@ def make_ep_local(w: Workload, ep: int, rows_per_expert: int, device="cpu") -> d
     return out
 
 
+def ep_receive_order(E_local: int, ep: int, C: int) -> np.ndarray:
+    """Row layout of a rank's receive buffer after a uniform all-to-all:
+    the ep sources' chunks follow one another, each holding the rank's
+    E_local experts x C rows, so received row src*E_local*C + e*C + c is
+    row c of local expert e from source src.  Returns, for the expert-major
+    slot s = e*(ep*C) + src*C + c, that received row (int32 [E_local*ep*C]):
+    a route list that reads the receive buffer in expert order."""
+    e, src, c = np.meshgrid(np.arange(E_local), np.arange(ep), np.arange(C), indexing="ij")
+    return (src * (E_local * C) + e * C + c).reshape(-1).astype(np.int32)
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Host uint16 view of a bf16 tensor's bit patterns."""
     return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)

@@ -67,3 +67,27 @@ def test_qwen_shape_ep8_share():
         idx = torch.as_tensor(rows, device="cuda")
         assert_bf16_close(host(act[idx]), r_act, f"act e{e}")
         assert_bf16_close(host(ro[idx]), r_out, f"route_out e{e}")
+
+
+def test_source_major_receive_buffer():
+    """After an all-to-all the receive buffer is source-major (each source's
+    chunk holds all local experts); the grouped FFN reads it in expert order
+    through a fixed route list, with the same results bit for bit as on the
+    expert-major copy."""
+    w = moe_inputs.WORKLOADS["qwen3_30b_a3b_n4096_h2048_e128_k8"]
+    ep = 8
+    Cs = oracle.source_capacity(w.N, w.K, w.E, w.F)
+    d = moe_inputs.make_ep_local(w, ep, Cs * ep, "cuda")
+    E, C = d["E"], d["C"]
+    perm = torch.as_tensor(moe_inputs.ep_receive_order(E, ep, Cs), device="cuda")
+    assert torch.equal(torch.sort(perm).values, torch.arange(E * C, dtype=torch.int32, device="cuda"))
+    x_recv = torch.empty_like(d["x"])
+    x_recv[perm.long()] = d["x"]                       # slot s's row sits at received row perm[s]
+    _, act_id, ro_id = _run(d)
+    act = torch.empty_like(act_id)
+    ro = torch.empty_like(ro_id)
+    moe_grouped_fc1_swiglu(x_recv, d["w1"], perm, d["probs"], C, act)
+    moe_grouped_fc2(act, d["w2"], E * C, C, ro)
+    torch.cuda.synchronize()
+    assert torch.equal(act, act_id) and torch.equal(ro, ro_id)
+

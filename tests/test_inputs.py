@@ -44,3 +44,15 @@ def test_skew_bias_profile():
 
 
 LOGITS_TINY_SHA256 = "815dc0e8486f29377791bf2a7d14cbfe5a312b06d5742ee87cbf5cbe672bad79"
+
+
+def test_ep_receive_order_is_the_source_major_layout():
+    El, ep, C = 3, 4, 5
+    p = moe_inputs.ep_receive_order(El, ep, C)
+    assert p.dtype == np.int32 and sorted(p.tolist()) == list(range(El * ep * C))
+    for e in range(El):
+        for src in range(ep):
+            for c in range(C):
+                # slot (e, src, c) in expert-major order reads source src's chunk
+                assert p[e * ep * C + src * C + c] == src * El * C + e * C + c
+

@@ -440,6 +440,12 @@ def bench_ep_local(args, w, torch, moe):
     us_sm = time_calls(torch, ["fc1_source_major"],
                        [lambda: moe.moe_grouped_fc1_swiglu(x_recv, d["w1"], perm, d["probs"], C, act_sm,
                                                            stream)], stream, args)["fc1_source_major"]
+    inv = torch.empty_like(perm)
+    inv[perm.long()] = torch.arange(N, dtype=torch.int32, device="cuda")
+    back = torch.empty_like(ro)
+    torch.cuda.synchronize()
+    us_back = time_calls(torch, ["return_reorder"],
+                         [lambda: moe.moe_dispatch_rows(ro, inv, back, stream)], stream, args)["return_reorder"]
     flops = {"fc1": 2.0 * N * 2 * I * H, "fc2": 2.0 * N * H * I}
     nbytes = {"fc1": E * 2 * I * H * 2 + N * H * 2 + N * 8 + N * I * 2,
               "fc2": E * H * I * 2 + N * I * 2 + N * H * 2}
@@ -486,6 +492,8 @@ def bench_ep_local(args, w, torch, moe):
                              nbytes["fc1"], us["fc1"]),
         # FC1 on the source-major receive buffer through its route list
         "fc1_source_major_us": us_sm,
+        # route_out back into source-major chunks for the return exchange
+        "return_reorder_us": us_back,
         # not part of the timed step: the source rank's send-buffer pack
         # before the exchange (moe_dispatch_rows), eager, HIP events
         "dispatch_rows": {"us": pack_us, "slot_rows": R, "algorithmic_bytes": pack_bytes,

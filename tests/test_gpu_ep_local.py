@@ -21,7 +21,7 @@ import torch
 import moe_inputs
 import oracle
 from gpu_support import assert_bf16_close, host, say
-from mixture_experts_expert_amd import moe_grouped_fc1_swiglu, moe_grouped_fc2
+from mixture_experts_expert_amd import moe_dispatch_rows, moe_grouped_fc1_swiglu, moe_grouped_fc2
 
 pytestmark = pytest.mark.gpu
 
@@ -90,4 +90,12 @@ def test_source_major_receive_buffer():
     moe_grouped_fc2(act, d["w2"], E * C, C, ro)
     torch.cuda.synchronize()
     assert torch.equal(act, act_id) and torch.equal(ro, ro_id)
+    # the return direction: route_out back into source-major chunks is the
+    # same row gather through the inverse list (received row j <- slot inv[j])
+    inv = torch.empty_like(perm)
+    inv[perm.long()] = torch.arange(E * C, dtype=torch.int32, device="cuda")
+    back = torch.empty_like(ro)
+    moe_dispatch_rows(ro, inv, back)
+    torch.cuda.synchronize()
+    assert torch.equal(back[perm.long()], ro)
 

@@ -446,6 +446,11 @@ def bench_ep_local(args, w, torch, moe):
     torch.cuda.synchronize()
     us_back = time_calls(torch, ["return_reorder"],
                          [lambda: moe.moe_dispatch_rows(ro, inv, back, stream)], stream, args)["return_reorder"]
+    # or FC2 writes its rows there directly through the row map
+    ro_map = torch.empty_like(ro)
+    us_map = time_calls(torch, ["fc2_rows"],
+                        [lambda: moe.moe_grouped_fc2_rows(act, d["w2"], perm, N, C, ro_map, stream)],
+                        stream, args)["fc2_rows"]
     flops = {"fc1": 2.0 * N * 2 * I * H, "fc2": 2.0 * N * H * I}
     nbytes = {"fc1": E * 2 * I * H * 2 + N * H * 2 + N * 8 + N * I * 2,
               "fc2": E * H * I * 2 + N * I * 2 + N * H * 2}
@@ -494,6 +499,8 @@ def bench_ep_local(args, w, torch, moe):
         "fc1_source_major_us": us_sm,
         # route_out back into source-major chunks for the return exchange
         "return_reorder_us": us_back,
+        # FC2 writing route_out straight into the source-major chunks
+        "fc2_rows_us": us_map,
         # not part of the timed step: the source rank's send-buffer pack
         # before the exchange (moe_dispatch_rows), eager, HIP events
         "dispatch_rows": {"us": pack_us, "slot_rows": R, "algorithmic_bytes": pack_bytes,

@@ -267,6 +267,21 @@ int moe_grouped_fc1_swiglu(const uint16_t* x, const uint16_t* w1, const int32_t*
 int moe_grouped_fc2(const uint16_t* act, const uint16_t* w2, int64_t N, int32_t H, int32_t I,
                     int32_t E, int64_t C, uint16_t* route_out, hipStream_t stream);
 
+/* FC2 with a row map: slot s's output row goes to route_out[out_rows[s]]
+ * instead of route_out[s] (same products, same bits).  For an
+ * expert-parallel rank: with out_rows the inverse of the receive-order route
+ * list, route_out leaves FC2 already in the source-major chunks the return
+ * all-to-all sends ([FC] Design notes: every chunk C rows per expert), with
+ * no reorder pass.
+ *   out_rows  in int32 [E*Cp]; an entry outside [0, E*Cp) drops that row.
+ *             Entries should name distinct rows (a repeated row receives one
+ *             of its slots' results); rows no entry names are left as they were.
+ * Other arguments as moe_grouped_fc2; additionally E*Cp*H*2 must stay below
+ * 2^31 bytes (MOE_ERR_UNSUPPORTED otherwise). */
+int moe_grouped_fc2_rows(const uint16_t* act, const uint16_t* w2, const int32_t* out_rows, int64_t N,
+                         int32_t H, int32_t I, int32_t E, int64_t C, uint16_t* route_out,
+                         hipStream_t stream);
+
 /* Step 5: contention-free gather-combine ([PF] sections 2 and 5,
  * route_gather_combine): y[t] = bf16( float32 sum over k = 0..K-1 with
  * token_routes[t,k] >= 0 of route_out[token_routes[t,k]] ), summed in k order

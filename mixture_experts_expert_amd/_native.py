@@ -53,6 +53,7 @@ _SIGNATURES = {
     "moe_grouped_fc1_swiglu": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64,
                                               _vp, _vp]),
     "moe_grouped_fc2": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _vp]),
+    "moe_grouped_fc2_rows": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp, _vp]),
     "moe_gather_combine": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i32, _i64, _vp, _vp]),
     "moe_dispatch_rows": (ctypes.c_int, [_vp, _vp, _i64, _i32, _i64, _vp, _vp]),
     "moe_grouped_fc1_swiglu_save": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
@@ -228,6 +229,15 @@ def moe_grouped_fc2(act, w2, N: int, C: int, route_out, stream=None):
     _check("moe_grouped_fc2", lib.moe_grouped_fc2(
         _ptr(act, torch.bfloat16, R * I, "act"), _ptr(w2, torch.bfloat16, E * H * I, "w2"),
         N, H, I, E, C, _ptr(route_out, torch.bfloat16, R * H, "route_out"), _stream(stream)))
+
+
+def moe_grouped_fc2_rows(act, w2, out_rows, N: int, C: int, route_out, stream=None):
+    E, H, I = w2.shape
+    R = E * moe_padded_capacity(C)
+    _check("moe_grouped_fc2_rows", lib.moe_grouped_fc2_rows(
+        _ptr(act, torch.bfloat16, R * I, "act"), _ptr(w2, torch.bfloat16, E * H * I, "w2"),
+        _ptr(out_rows, torch.int32, R, "out_rows"), N, H, I, E, C,
+        _ptr(route_out, torch.bfloat16, R * H, "route_out"), _stream(stream)))
 
 
 def moe_gather_combine(route_out, token_routes, y, stream=None):

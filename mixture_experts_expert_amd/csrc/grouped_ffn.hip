@@ -655,7 +655,7 @@ int pick_tile_dyn(double mean) {
 // loading waves never wait on the route_out stores (same tiles, same K
 // order, the same results bit for bit as the one-role kernel, a few percent
 // faster).
-int launch_fc2_slots(const FfnArgs& a, int E, hipStream_t s) {
+int launch_fc2_slots(const FfnArgs& a, int E, hipStream_t s, const int* out_rows = nullptr) {
     SlotArgs sa{};
     sa.a = a.a; sa.b = a.w; sa.out = a.out;
     sa.lda = a.Kdim; sa.ldb = a.Kdim; sa.ldo = a.ncols;
@@ -667,7 +667,12 @@ int launch_fc2_slots(const FfnArgs& a, int E, hipStream_t s) {
     sa.tiles = static_cast<int>(tiles);
     sa.b_estride = static_cast<int64_t>(a.wrows) * a.Kdim;
     sa.krot = kKRotate;
-    slot_gemm_kernel<false><<<std::min(sa.tiles, device_cus()), 12 * kWave, 0, s>>>(sa);
+    if (out_rows) {
+        sa.out_rows = out_rows;
+        slot_gemm_kernel<false, true><<<std::min(sa.tiles, device_cus()), 12 * kWave, 0, s>>>(sa);
+    } else {
+        slot_gemm_kernel<false><<<std::min(sa.tiles, device_cus()), 12 * kWave, 0, s>>>(sa);
+    }
     return MOE_OK;
 }
 
@@ -781,6 +786,22 @@ extern "C" int moe_grouped_fc2(const uint16_t* act, const uint16_t* w2, int64_t 
     st = check_ptrs({act, w2, route_out});
     if (st != MOE_OK) return st;
     st = launch(fc2_args(act, w2, N, H, I, Cp, route_out), false, E, stream);
+    return st != MOE_OK ? st : launch_status();
+}
+
+extern "C" int moe_grouped_fc2_rows(const uint16_t* act, const uint16_t* w2, const int32_t* out_rows,
+                                    int64_t N, int32_t H, int32_t I, int32_t E, int64_t C,
+                                    uint16_t* route_out, hipStream_t stream) {
+    using namespace moe;
+    int Cp = 0;
+    int st = check_ffn(N, H, I, E, C, &Cp);
+    if (st != MOE_OK) return st;
+    if (N == 0 || C == 0) return MOE_OK;
+    // the mapped rows address the whole output through one 32-bit descriptor
+    if (static_cast<int64_t>(E) * Cp * H * 2 >= (static_cast<int64_t>(1) << 31)) return MOE_ERR_UNSUPPORTED;
+    st = check_ptrs({act, w2, out_rows, route_out});
+    if (st != MOE_OK) return st;
+    st = launch_fc2_slots(fc2_args(act, w2, N, H, I, Cp, route_out), E, stream, out_rows);
     return st != MOE_OK ? st : launch_status();
 }
 

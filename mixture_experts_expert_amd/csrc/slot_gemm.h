@@ -4,7 +4,9 @@
 //
 // with A route-ordered (row s of expert e's segment seg = e*Cp) and B_e expert
 // e's weight matrix, stored N-major ([Nn][Kd], FC2's W2 in the forward) or
-// K-major ([Kd][Nn], the transposed-weight view of a dgrad).
+// K-major ([Kd][Nn], the transposed-weight view of a dgrad).  With a row map
+// the output row of slot seg + s is out_rows[seg + s] instead (any row of
+// the E*Cp-row output; entries outside it drop the row).
 //
 // [PF] "Permute-Free Grouped GEMM for MoE (bf16, gfx950)", sections 3 and 5:
 // FC2 of the forward (A = act by route position) and the FC1 data gradient
@@ -30,6 +32,7 @@ struct SlotArgs {
     const uint16_t* a;            // A rows (row-major, K contiguous)
     const uint16_t* b;            // expert weights, b_estride elements apart
     uint16_t* out;                // [E*Cp, ldo]
+    const int* out_rows;          // row map (ROWMAP only): slot -> output row
     int lda, ldb, ldo;            // row pitches in elements
     int Nn, Kd;                   // output columns, contraction length
     int Cp;                       // slots per expert
@@ -38,7 +41,7 @@ struct SlotArgs {
     int krot;                     // expert e starts its K walk at slab (e*krot) % KT
 };
 
-template <bool BKM>
+template <bool BKM, bool ROWMAP = false>
 __global__ __launch_bounds__(768) void slot_gemm_kernel(SlotArgs p) {
     constexpr int BMT = 256, BNT = 256, BK = 64, WM = 2, WN = 4, NA = 2, NB = 3;
     constexpr int NC = WM * WN;                    // consumer waves
@@ -183,7 +186,18 @@ __global__ __launch_bounds__(768) void slot_gemm_kernel(SlotArgs p) {
             for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
     __syncthreads();
     int tc = t0, ktc = 0, a_rd = 0, b_rd = 0;
+    int orow[MI];                                  // ROWMAP: the output rows of the lane's slots
     for (int g = 0; g < S; ++g) {
+        if (ROWMAP && ktc == 0) {
+            // fetched at the tile's first step, used at its end
+            const int rest = tc / p.NT;
+            const int e = rest / p.MT, m0 = (rest % p.MT) * BMT;
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const int row = m0 + wm * WTM + mi * 32 + (lane & 31);
+                orow[mi] = row < len ? p.out_rows[static_cast<int64_t>(e) * p.Cp + row] : -1;
+            }
+        }
         const uint8_t* sA = smem + a_rd;
         const lds_u8* sB = (const lds_u8*)smem + B_RING + b_rd;
 #pragma unroll
@@ -217,11 +231,19 @@ __global__ __launch_bounds__(768) void slot_gemm_kernel(SlotArgs p) {
             // offset beyond the descriptor: the store is dropped.
             const int nt = tc % p.NT, rest = tc / p.NT;
             const int e = rest / p.MT, m0 = (rest % p.MT) * BMT;
+            // the output rows: the expert's segment, or (ROWMAP) the whole
+            // E*Cp-row output, whose size the host keeps below 2^31 bytes
+            const int rows_out = p.tiles / (p.MT * p.NT) * p.Cp;
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
-                p.out + static_cast<int64_t>(e) * p.Cp * p.ldo, static_cast<short>(0), len * p.ldo * 2, kRsrcWord3);
+                ROWMAP ? p.out : p.out + static_cast<int64_t>(e) * p.Cp * p.ldo, static_cast<short>(0),
+                (ROWMAP ? rows_out : len) * p.ldo * 2, kRsrcWord3);
 #pragma unroll
             for (int mi = 0; mi < MI; ++mi) {
-                const int row = m0 + wm * WTM + mi * 32 + (lane & 31);
+                // the lane's output row: its slot within the segment, or the
+                // mapped row of the whole output (live if inside it)
+                const int row = ROWMAP ? orow[mi] : m0 + wm * WTM + mi * 32 + (lane & 31);
+                const bool row_live = ROWMAP ? static_cast<unsigned>(row) < static_cast<unsigned>(rows_out)
+                                             : row < len;
 #pragma unroll
                 for (int ni = 0; ni < NI; ++ni) {
                     uint32_t gq[4][2];
@@ -237,7 +259,7 @@ __global__ __launch_bounds__(768) void slot_gemm_kernel(SlotArgs p) {
                         u32x4 d;
                         d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
                         const int col = nt * BNT + wn * WTN + ni * 32 + 16 * q + 8 * half;
-                        const uint32_t off = row < len && col < p.Nn
+                        const uint32_t off = row_live && col < p.Nn
                             ? (static_cast<uint32_t>(row) * p.ldo + col) * 2u : kOob;
                         __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
                     }

@@ -26,7 +26,8 @@ def test_every_declared_symbol_is_exported():
                           "moe_gather_combine", "moe_grouped_fc1_swiglu_save",
                           "moe_grouped_fc2_dgrad", "moe_swiglu_bwd", "moe_grouped_fc1_dgrad",
                           "moe_grouped_fc2_wgrad", "moe_grouped_fc1_wgrad", "moe_route_bwd",
-                          "moe_route_dropless_live", "moe_dispatch_rows"}
+                          "moe_route_dropless_live", "moe_dispatch_rows",
+                          "moe_grouped_fc2_rows"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -158,6 +159,18 @@ def test_combine_validation():
     assert f(ALIGNED, ALIGNED, 16, 2, 72, 128, ALIGNED, NUL) == UNSUPPORTED
     assert f(ALIGNED, MIS, 16, 2, 64, 128, ALIGNED, NUL) == MISALIGNED
     assert f(NUL, NUL, 0, 2, 64, 0, NUL, NUL) == OK
+
+
+def test_fc2_rows_validation():
+    f = lib.moe_grouped_fc2_rows
+    A = ALIGNED
+    assert f(A, A, A, -1, 64, 64, 4, 8, A, NUL) == INVALID
+    assert f(A, A, A, 16, 72, 64, 4, 8, A, NUL) == UNSUPPORTED
+    assert f(A, A, NUL, 16, 64, 64, 4, 8, A, NUL) == INVALID
+    assert f(A, A, MIS, 16, 64, 64, 4, 8, A, NUL) == MISALIGNED
+    # the whole output past 2^31 bytes: 1024 experts x 128 slots x 8192 x 2
+    assert f(A, A, A, 16, 8192, 64, 1024, 128, A, NUL) == UNSUPPORTED
+    assert f(NUL, NUL, NUL, 0, 64, 64, 4, 8, NUL, NUL) == OK   # no tokens
 
 
 def test_dispatch_rows_validation():

@@ -21,7 +21,8 @@ import torch
 import moe_inputs
 import oracle
 from gpu_support import assert_bf16_close, host, say
-from mixture_experts_expert_amd import moe_dispatch_rows, moe_grouped_fc1_swiglu, moe_grouped_fc2
+from mixture_experts_expert_amd import (moe_dispatch_rows, moe_grouped_fc1_swiglu, moe_grouped_fc2,
+                                        moe_grouped_fc2_rows)
 
 pytestmark = pytest.mark.gpu
 
@@ -98,4 +99,36 @@ def test_source_major_receive_buffer():
     moe_dispatch_rows(ro, inv, back)
     torch.cuda.synchronize()
     assert torch.equal(back[perm.long()], ro)
+    # or FC2 writes them there itself through the row map (no reorder pass)
+    ro_map = torch.full_like(ro, float("nan"))
+    moe_grouped_fc2_rows(act, d["w2"], perm, E * C, C, ro_map)
+    torch.cuda.synchronize()
+    assert torch.equal(ro_map, back)
+
+
+def test_fc2_row_map_identity_and_drops():
+    """The identity map reproduces plain FC2 bit for bit; entries outside
+    the output drop their rows and leave those rows untouched."""
+    w = moe_inputs.Workload("fc2_rows_small", 64, 320, 8, 2, 1.0, 192, 23)
+    d = moe_inputs.make_ep_local(w, 2, 512, "cuda")         # 4 experts x 512 rows (two row tiles)
+    _, act, ro = _run(d)
+    E, C = d["E"], d["C"]
+    R = E * C
+    ident = torch.arange(R, dtype=torch.int32, device="cuda")
+    out = torch.full_like(ro, float("nan"))
+    moe_grouped_fc2_rows(act, d["w2"], ident, R, C, out)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ro)
+    rng = np.random.default_rng(5)
+    dropped = torch.as_tensor(np.sort(rng.choice(R, 100, replace=False)), device="cuda")
+    bad = ident.clone()
+    bad[dropped[:50]] = -1
+    bad[dropped[50:]] = R
+    out = torch.full_like(ro, 7.0)
+    moe_grouped_fc2_rows(act, d["w2"], bad, R, C, out)
+    torch.cuda.synchronize()
+    keep = torch.ones(R, dtype=torch.bool, device="cuda")
+    keep[dropped] = False
+    assert torch.equal(out[keep], ro[keep])
+    assert torch.all(out[~keep] == 7.0)
 

@@ -5,9 +5,9 @@ Each source routes its own N/ep tokens over all E experts (capacity from its
 own N, every source selects), packs its send buffer with moe_dispatch_rows
 and runs its single-GPU forward as the reference.  Rank r receives, from
 every source, the segment of its E/ep experts (source-major), runs the
-grouped FFN through the receive-order route list, and reorders route_out
-back into source-major chunks with moe_dispatch_rows through the inverse
-list.  Each source then gathers its routes from the returned rows with
+grouped FFN through the receive-order route list, and gets route_out back
+in source-major chunks either from FC2's row map (even ranks) or by a
+reorder with moe_dispatch_rows through the inverse list (odd ranks).  Each source then gathers its routes from the returned rows with
 moe_gather_combine.  Its y must equal its own single-GPU forward within the
 forward's bars (the ranks' launches walk K from a different starting slab,
 so the float32 sums are reordered), and the pad rows and dropped routes
@@ -21,7 +21,7 @@ import torch
 import moe_inputs
 from gpu_support import assert_bf16_close, host, run_steps, say
 from mixture_experts_expert_amd import (MoEBuffers, moe_dispatch_rows, moe_gather_combine,
-                                        moe_grouped_fc1_swiglu, moe_grouped_fc2)
+                                        moe_grouped_fc1_swiglu, moe_grouped_fc2, moe_grouped_fc2_rows)
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -58,9 +58,12 @@ def test_ep_emulated_equals_single_gpu_forward(ep):
         act = torch.empty(ep * seg, I, dtype=torch.bfloat16, device=DEV)
         ro = torch.empty(ep * seg, H, dtype=torch.bfloat16, device=DEV)
         moe_grouped_fc1_swiglu(recv, w1, perm, probs, ep * Cp, act)
-        moe_grouped_fc2(act, w2, ep * seg, ep * Cp, ro)
         back = torch.empty_like(ro)
-        moe_dispatch_rows(ro, inv, back)                      # source-major again
+        if r % 2 == 0:
+            moe_grouped_fc2_rows(act, w2, perm, ep * seg, ep * Cp, back)   # straight to source-major
+        else:
+            moe_grouped_fc2(act, w2, ep * seg, ep * Cp, ro)
+            moe_dispatch_rows(ro, inv, back)                  # source-major again
         for s in range(ep):                                   # the return all-to-all
             returned[s][part] = back[s * seg:(s + 1) * seg]
     torch.cuda.synchronize()

@@ -4,12 +4,16 @@
 
 Every source under csrc/ is compiled to a gfx950 code object with packed
 fp32 instructions disabled, then linked into one shared library next to this
-file.  The build always recompiles.
+file.  The build always recompiles, and records a hash of the sources it
+compiled (every csrc/ and include/ file, and the compiler flags) in
+libmoe_native.so.srchash, so a library older than its sources can be told
+apart from a current one (``is_stale``).
 """
 
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -20,6 +24,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_native.so")
+STAMP = LIB + ".srchash"
+INCLUDE = os.path.join(ROOT, "include")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -41,6 +47,28 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def source_hash() -> str:
+    """sha256 (16 hex digits) of every library source and header, by name and
+    content, plus the compiler flags."""
+    h = hashlib.sha256(" ".join(HIPCC_FLAGS[1:]).encode())
+    for d in (CSRC, INCLUDE):
+        for f in sorted(os.listdir(d)):
+            if f.endswith((".hip", ".h")):
+                h.update(f.encode())
+                with open(os.path.join(d, f), "rb") as fh:
+                    h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def is_stale() -> bool:
+    """True when the library is missing or was built from other sources."""
+    try:
+        with open(STAMP) as fh:
+            return not os.path.exists(LIB) or fh.read().strip() != source_hash()
+    except OSError:
+        return True
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
@@ -53,6 +81,7 @@ def _compile(src: str) -> str:
 def build(verbose: bool = True) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
+    digest = source_hash()
     workers = max(1, min(len(srcs), 8))
     with cf.ThreadPoolExecutor(workers) as ex:
         objs = list(ex.map(_compile, srcs))
@@ -62,6 +91,8 @@ def build(verbose: bool = True) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    with open(STAMP, "w") as fh:
+        fh.write(digest + "\n")
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
     return LIB

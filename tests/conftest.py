@@ -10,13 +10,17 @@ if ROOT not in sys.path:
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
-# The suite loads the in-tree library; it builds it only when nothing is built.
-if not os.path.exists(os.path.join(ROOT, "mixture_experts_expert_amd", "libmoe_native.so")):
-    import importlib.util as _ilu   # the package itself refuses to import unbuilt
-    _spec = _ilu.spec_from_file_location(
-        "_moe_build", os.path.join(ROOT, "mixture_experts_expert_amd", "build.py"))
-    _build = _ilu.module_from_spec(_spec)
-    _spec.loader.exec_module(_build)
+# The suite loads the in-tree library.  It rebuilds it when nothing is built or
+# when the sources changed since the last build (the hash the build records
+# beside the library differs), so a stale library is never tested.
+import importlib.util as _ilu   # the package itself refuses to import unbuilt
+
+_spec = _ilu.spec_from_file_location(
+    "_moe_build", os.path.join(ROOT, "mixture_experts_expert_amd", "build.py"))
+_build = _ilu.module_from_spec(_spec)
+_spec.loader.exec_module(_build)
+if _build.is_stale():
+    print("conftest: libmoe_native.so is missing or older than its sources; rebuilding", flush=True)
     _build.build(verbose=True)
 
 

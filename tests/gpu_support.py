@@ -60,6 +60,19 @@ def assert_bf16_close(gpu_bits, ref, what):
     return nr
 
 
+def bf16_close_stats(gpu_bits, ref_bits):
+    """The forward's bars, quietly: elements outside ATOL + RTOL*|ref|, the
+    normwise relative error, the largest absolute error and the share of
+    bit-equal elements (both sides bf16 bit patterns)."""
+    g = oracle.bf16_bits_to_f64(gpu_bits)
+    r = oracle.bf16_bits_to_f64(ref_bits)
+    d = np.abs(g - r)
+    return {"bad": int((d > ATOL + RTOL * np.abs(r)).sum()),
+            "norm": float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)),
+            "max_abs": float(d.max(initial=0.0)),
+            "exact": float(np.mean(g == r)) if g.size else 1.0}
+
+
 def check_routing(buf: MoEBuffers, lg: np.ndarray, K: int):
     """S1 bit-exact against the oracle on the same logits."""
     ids, probs = oracle.route_topk(lg, K)

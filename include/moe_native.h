@@ -96,6 +96,19 @@ int64_t moe_padded_capacity(int64_t C);
  * dropless expert_ids has (this)/BM entries.  <0 on bad arguments. */
 int64_t moe_dropless_bound(int64_t N, int32_t K, int32_t E);
 
+/* Workspace of the routing calls (moe_route_capacity, moe_route_capacity_align,
+ * moe_route_dropless, moe_route_dropless_live): the routing map ([PF]
+ * section 4 builds the layout from the routing map), expert-major with rows
+ * of Np = N rounded up to a multiple of 16 tokens -- first E*Np bytes, byte
+ * [e*Np + t] = k+1 when token t's pick k is expert e, else 0; then E*Np
+ * float32 words holding each pick's probability at the same position.
+ * Returns 5*E*Np, or 0 when the arguments fall outside the routing envelope.
+ * Host-only.  The workspace is a device buffer of at least this many bytes,
+ * 16-byte aligned, owned by the caller; each call overwrites it (its
+ * contents between calls mean nothing), so calls that share one workspace
+ * must not overlap. */
+size_t moe_route_capacity_workspace_bytes(int64_t N, int32_t E, int32_t K);
+
 /* Steps 1-2: top-K softmax routing and fixed-capacity drop-and-pad
  * selection ([FC] Design notes; [PF] section 4, route_counts/route_within).
  *
@@ -108,13 +121,18 @@ int64_t moe_dropless_bound(int64_t N, int32_t K, int32_t E);
  *   route_slot   out  int32   [N, K]  slot of route (t,k) inside its expert's
  *                                     segment, or -1 if the route is dropped
  *   expert_count out  int32   [E]     kept routes per expert = min(C, load)
+ *   workspace    scratch               moe_route_capacity_workspace_bytes(N, E, K)
+ *                                     bytes (MOE_ERR_INVALID_ARG if null or
+ *                                     smaller, MOE_ERR_MISALIGNED if not
+ *                                     16-byte aligned)
  *
  * Per expert, the min(C, load) routes with the largest topk_probs are kept
  * (equal probabilities: lower token first); kept routes take slots
  * 0..count-1 in ascending token order. */
 int moe_route_capacity(const float* logits, int64_t N, int32_t E, int32_t K, int64_t C,
                        int32_t* topk_ids, float* topk_probs, int32_t* route_slot,
-                       int32_t* expert_count, hipStream_t stream);
+                       int32_t* expert_count, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 /* Step 3: sync-free align ([PF] section 4, Data structures; section 5,
  * route_list_align), fixed-capacity form: expert e owns slots
@@ -139,7 +157,8 @@ int moe_align(const int32_t* topk_ids, const float* topk_probs, const int32_t* r
 /* Steps 1-3 in one call: moe_route_capacity followed by moe_align, with the
  * selection workgroup of each expert writing its own segment of the route
  * list and the token_routes entries of its routes (sources as above).  Same
- * arguments as the two calls together, same outputs bit for bit; the
+ * arguments as the two calls together (with moe_route_capacity's
+ * workspace), same outputs bit for bit; the
  * per-token kept counts are accumulated with integer atomics (order-free),
  * so the result is deterministic. */
 int moe_route_capacity_align(const float* logits, int64_t N, int32_t E, int32_t K, int64_t C,
@@ -147,7 +166,7 @@ int moe_route_capacity_align(const float* logits, int64_t N, int32_t E, int32_t 
                              int32_t* expert_count, int32_t* sorted_slot_ids, float* slot_probs,
                              int32_t* expert_ids, int32_t* block_start, int32_t* token_routes,
                              int32_t* token_route_count, int32_t* num_tokens_post_padded,
-                             hipStream_t stream);
+                             void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Dropless variant of steps 1-3 ([PF] sections 4-5: route_list_scan and
  * route_list_align over the routing map, with no capacity): top-K routing as
@@ -175,12 +194,14 @@ int moe_route_capacity_align(const float* logits, int64_t N, int32_t E, int32_t 
  *                                     padded segments), a device scalar
  *
  * Within-expert order (token order) and the pad contents follow the
- * fixed-capacity form.  Same validation as moe_route_capacity (no C). */
+ * fixed-capacity form.  Same validation and workspace as moe_route_capacity
+ * (no C). */
 int moe_route_dropless(const float* logits, int64_t N, int32_t E, int32_t K, int32_t* topk_ids,
                        float* topk_probs, int32_t* route_within, int32_t* route_counts,
                        int32_t* sorted_slot_ids, float* slot_probs, int32_t* expert_ids,
                        int32_t* block_start, int32_t* token_routes, int32_t* token_route_count,
-                       int32_t* num_tokens_post_padded, hipStream_t stream);
+                       int32_t* num_tokens_post_padded, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream);
 
 /* moe_route_dropless for a variable number of live tokens, read on the
  * device: [BK] "What this adds" (one shape is captured and every smaller
@@ -207,7 +228,7 @@ int moe_route_dropless_live(const float* logits, int64_t N, int32_t E, int32_t K
                             int32_t* sorted_slot_ids, float* slot_probs, int32_t* expert_ids,
                             int32_t* block_start, int32_t* token_routes,
                             int32_t* token_route_count, int32_t* num_tokens_post_padded,
-                            hipStream_t stream);
+                            void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Step 4 over the dropless route list: the same FC1 -> SwiGLU*prob -> FC2
  * as moe_grouped_ffn_fwd, with expert e's rows the slots

@@ -32,11 +32,13 @@ from ._native import (  # noqa: F401
     moe_route_bwd,
     moe_route_capacity,
     moe_route_capacity_align,
+    moe_route_capacity_workspace_bytes,
     moe_route_dropless,
     moe_route_dropless_live,
     moe_source_capacity,
     moe_status_string,
     moe_swiglu_bwd,
+    route_workspace,
 )
 from .serving import BucketLadder, ServingLadder  # noqa: F401
 from .forward import (  # noqa: F401

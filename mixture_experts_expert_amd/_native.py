@@ -35,17 +35,22 @@ _SIGNATURES = {
     "moe_layout_block_m": (_i32, []),
     "moe_padded_capacity": (_i64, [_i64]),
     "moe_dropless_bound": (_i64, [_i64, _i32, _i32]),
-    "moe_route_dropless": (ctypes.c_int, [_vp, _i64, _i32, _i32] + [_vp] * 12),
-    "moe_route_dropless_live": (ctypes.c_int, [_vp, _i64, _i32, _i32] + [_vp] * 13),
+    "moe_route_capacity_workspace_bytes": (ctypes.c_size_t, [_i64, _i32, _i32]),
+    "moe_route_dropless": (ctypes.c_int, [_vp, _i64, _i32, _i32] + [_vp] * 11
+                           + [_vp, ctypes.c_size_t, _vp]),
+    "moe_route_dropless_live": (ctypes.c_int, [_vp, _i64, _i32, _i32] + [_vp] * 12
+                                + [_vp, ctypes.c_size_t, _vp]),
     "moe_grouped_ffn_fwd_dropless": (ctypes.c_int, [_vp] * 7 + [_i64, _i32, _i32, _i32, _i32,
                                                                 _vp, _vp, _vp]),
     "moe_grouped_fc1_swiglu_dropless": (ctypes.c_int, [_vp] * 6 + [_i64, _i32, _i32, _i32, _i32,
                                                                    _vp, _vp]),
     "moe_grouped_fc2_dropless": (ctypes.c_int, [_vp] * 4 + [_i64, _i32, _i32, _i32, _i32,
                                                             _vp, _vp]),
-    "moe_route_capacity": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp, _vp]),
+    "moe_route_capacity": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
+                                          _vp, ctypes.c_size_t, _vp]),
     "moe_route_capacity_align": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
-                                                _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+                                                _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                                _vp, ctypes.c_size_t, _vp]),
     "moe_align": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i64,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_grouped_ffn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64,
@@ -116,6 +121,24 @@ def moe_dropless_bound(N: int, K: int, E: int) -> int:
     return r
 
 
+def moe_route_capacity_workspace_bytes(N: int, E: int, K: int) -> int:
+    b = int(lib.moe_route_capacity_workspace_bytes(int(N), int(E), int(K)))
+    if b == 0 and N > 0:
+        raise MoEError("moe_route_capacity_workspace_bytes", -2)
+    return b
+
+
+def route_workspace(N: int, E: int, K: int, device="cuda") -> torch.Tensor:
+    """A device workspace for the routing calls (uint8, 16-byte aligned)."""
+    return torch.empty(max(moe_route_capacity_workspace_bytes(N, E, K), 16), dtype=torch.uint8,
+                       device=device)
+
+
+def _ws(workspace, N: int, E: int, K: int):
+    need = moe_route_capacity_workspace_bytes(N, E, K)
+    return _ptr(workspace, torch.uint8, need, "workspace"), ctypes.c_size_t(workspace.numel())
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -142,19 +165,21 @@ def _check(fn: str, status: int):
 
 
 def moe_route_capacity(logits, K: int, C: int, topk_ids, topk_probs, route_slot, expert_count,
-                       stream=None):
+                       workspace, stream=None):
     N, E = logits.shape
     _check("moe_route_capacity", lib.moe_route_capacity(
         _ptr(logits, torch.float32, N * E, "logits"), N, E, K, C,
         _ptr(topk_ids, torch.int32, N * K, "topk_ids"),
         _ptr(topk_probs, torch.float32, N * K, "topk_probs"),
         _ptr(route_slot, torch.int32, N * K, "route_slot"),
-        _ptr(expert_count, torch.int32, E, "expert_count"), _stream(stream)))
+        _ptr(expert_count, torch.int32, E, "expert_count"), *_ws(workspace, N, E, K),
+        _stream(stream)))
 
 
 def moe_route_capacity_align(logits, K: int, C: int, topk_ids, topk_probs, route_slot,
                              expert_count, sorted_slot_ids, slot_probs, expert_ids, block_start,
-                             token_routes, token_route_count, num_tokens_post_padded, stream=None):
+                             token_routes, token_route_count, num_tokens_post_padded, workspace,
+                             stream=None):
     N, E = logits.shape
     R = E * moe_padded_capacity(C)
     BM = moe_layout_block_m()
@@ -170,7 +195,8 @@ def moe_route_capacity_align(logits, K: int, C: int, topk_ids, topk_probs, route
         _ptr(block_start, torch.int32, E, "block_start"),
         _ptr(token_routes, torch.int32, N * K, "token_routes"),
         _ptr(token_route_count, torch.int32, N, "token_route_count"),
-        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"), _stream(stream)))
+        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"),
+        *_ws(workspace, N, E, K), _stream(stream)))
 
 
 def moe_align(topk_ids, topk_probs, route_slot, expert_count, N: int, E: int, K: int, C: int,
@@ -259,7 +285,7 @@ def moe_dispatch_rows(x, sorted_slot_ids, rows, stream=None):
 
 def moe_route_dropless(logits, K: int, topk_ids, topk_probs, route_within, route_counts,
                        sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
-                       token_route_count, num_tokens_post_padded, stream=None):
+                       token_route_count, num_tokens_post_padded, workspace, stream=None):
     N, E = logits.shape
     R = moe_dropless_bound(N, K, E)
     BM = moe_layout_block_m()
@@ -275,12 +301,14 @@ def moe_route_dropless(logits, K: int, topk_ids, topk_probs, route_within, route
         _ptr(block_start, torch.int32, E, "block_start"),
         _ptr(token_routes, torch.int32, N * K, "token_routes"),
         _ptr(token_route_count, torch.int32, N, "token_route_count"),
-        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"), _stream(stream)))
+        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"),
+        *_ws(workspace, N, E, K), _stream(stream)))
 
 
 def moe_route_dropless_live(logits, K: int, n_live, topk_ids, topk_probs, route_within,
                             route_counts, sorted_slot_ids, slot_probs, expert_ids, block_start,
-                            token_routes, token_route_count, num_tokens_post_padded, stream=None):
+                            token_routes, token_route_count, num_tokens_post_padded, workspace,
+                            stream=None):
     N, E = logits.shape
     R = moe_dropless_bound(N, K, E)
     BM = moe_layout_block_m()
@@ -297,7 +325,8 @@ def moe_route_dropless_live(logits, K: int, n_live, topk_ids, topk_probs, route_
         _ptr(block_start, torch.int32, E, "block_start"),
         _ptr(token_routes, torch.int32, N * K, "token_routes"),
         _ptr(token_route_count, torch.int32, N, "token_route_count"),
-        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"), _stream(stream)))
+        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"),
+        *_ws(workspace, N, E, K), _stream(stream)))
 
 
 def moe_grouped_ffn_fwd_dropless(x, w1, w2, sorted_slot_ids, slot_probs, block_start,

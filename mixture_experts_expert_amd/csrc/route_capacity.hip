@@ -9,6 +9,8 @@
 //      ranks from one scan.
 #include <math.h>
 
+#include <algorithm>
+#include <atomic>
 #include <initializer_list>
 
 #include "moe_common.h"
@@ -24,6 +26,16 @@ namespace {
 // the K-way softmax runs in float64: exp(l_k - l_0), a sum in k order that
 // every lane forms identically through shuffles, one division, one rounding
 // to float32.
+//
+// The kernel also writes the routing map ([PF] section 4 builds its layout
+// from the routing map), expert-major: byte map[e * Np + t] = k + 1 if token
+// t's pick k is expert e, else 0 (Np = N rounded up to 16, every byte of
+// [0, Np) written each call), and beside it pmap[e * Np + t] = that pick's
+// probability (written at the picks only; elsewhere stale and never read).
+// A workgroup's TPB tokens form one TPB-byte piece of each expert's map row,
+// assembled in LDS and stored whole, so an expert's selection later reads
+// only its own rows -- picks and probabilities in one round trip -- instead
+// of every pick.
 // ---------------------------------------------------------------------------
 constexpr int kTopkThreads = 256;
 
@@ -49,53 +61,86 @@ __device__ __forceinline__ double dpp(double v) {
     return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<uint32_t>(lo));
 }
 
-// (value, expert) arg-max step: the partner wins if its value is larger, or
-// equal with a lower expert index; INT32_MAX marks "no candidate".
-__device__ __forceinline__ void argmax_step(float& bv, int& bi, float ov, int oi) {
-    const bool better = oi != INT32_MAX && (bi == INT32_MAX || ov > bv || (ov == bv && oi < bi));
-    if (better) { bv = ov; bi = oi; }
+// Arg-max key of (logit, expert): the float's bits made monotonic as an
+// unsigned integer in the high word (with -0 folded onto +0 first, so equal
+// logits stay equal), and ~expert in the low word, so the larger key is the
+// larger logit and, between equal logits, the lower expert -- the order the
+// routing defines, decided by one unsigned comparison with no branches.  Any
+// real logit's key exceeds 2^32; a key with a zero high word has been picked.
+__device__ __forceinline__ uint64_t topk_key(float v, int e) {
+    const uint32_t b = __float_as_uint(v + 0.0f);
+    const uint32_t u = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return (static_cast<uint64_t>(u) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
 }
+__device__ __forceinline__ float key_logit(uint64_t key) {
+    const uint32_t u = static_cast<uint32_t>(key >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
+}
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp64(uint64_t v) {
+    const int lo = dpp<CTRL>(static_cast<int>(v)), hi = dpp<CTRL>(static_cast<int>(v >> 32));
+    return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t v, int off, int width) {
+    const int lo = __shfl_xor(static_cast<int>(v), off, width);
+    const int hi = __shfl_xor(static_cast<int>(v >> 32), off, width);
+    return (static_cast<uint64_t>(static_cast<uint32_t>(hi)) << 32) | static_cast<uint32_t>(lo);
+}
+
+// Largest E each group width serves (see dispatch_topk), hence the LDS piece
+// of the routing map: E rows of TPB bytes.
+template <int LPT>
+constexpr int topk_max_e() { return LPT == 16 ? 128 : LPT == 32 ? 256 : kMaxE; }
 
 template <int LPT, int VPL>
 __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
     const float* __restrict__ logits, int N, int E, int K, int* __restrict__ topk_ids,
-    float* __restrict__ topk_probs, int* __restrict__ zero_count, const int* __restrict__ n_live) {
+    float* __restrict__ topk_probs, int* __restrict__ zero_count, const int* __restrict__ n_live,
+    uint8_t* __restrict__ map, uint32_t* __restrict__ pmap, int Np) {
     constexpr int TPB = kTopkThreads / LPT;   // tokens per block
+    constexpr int MAP_WORDS = topk_max_e<LPT>() * TPB / 4;
+    __shared__ uint32_t s_map[MAP_WORDS];
     const int g = threadIdx.x % LPT;          // lane within the token's group
-    const int t = blockIdx.x * TPB + threadIdx.x / LPT;
+    const int tl = threadIdx.x / LPT;         // token within the block
+    const int t = blockIdx.x * TPB + tl;
+    for (int i = threadIdx.x; i < E * TPB / 4; i += kTopkThreads) s_map[i] = 0u;
     // n_live (optional, device data, clamped to [0, N]): tokens at or past it
     // route nowhere -- expert -1, probability 0 -- and their logits are not read
     const int nl = n_live ? min(max(n_live[0], 0), N) : N;
     const bool live_token = t < nl;           // whole groups share t, so exchanges stay in-group
     const float* row = logits + static_cast<size_t>(live_token ? t : 0) * E;
-    float v[VPL];
+    uint64_t key[VPL];                        // 0 = no expert there
 #pragma unroll
     for (int j = 0; j < VPL; ++j) {
         const int e = j * LPT + g;
-        v[j] = (live_token && e < E) ? row[e] : 0.0f;
+        key[j] = (live_token && e < E) ? topk_key(row[e], e) : 0ull;
     }
-    uint32_t taken = 0;
     float my_logit = 0.0f;
     int my_id = 0;
     for (int k = 0; k < K; ++k) {
-        float bv = 0.0f;
-        int bi = INT32_MAX;
+        // the lane's best remaining key (a tree for independent comparisons),
+        // then the group's, by DPP inside 16-lane rows and shuffles across them
+        uint64_t m[VPL];
 #pragma unroll
-        for (int j = 0; j < VPL; ++j) {
-            const int e = j * LPT + g;
-            const bool live = e < E && !((taken >> j) & 1u);
-            if (live && (bi == INT32_MAX || v[j] > bv)) { bv = v[j]; bi = e; }
-        }
-        // all-reduce over the 16-lane row with DPP, then across rows
-        argmax_step(bv, bi, dpp<kDppXor1>(bv), dpp<kDppXor1>(bi));
-        argmax_step(bv, bi, dpp<kDppXor2>(bv), dpp<kDppXor2>(bi));
-        argmax_step(bv, bi, dpp<kDppHalfMirror>(bv), dpp<kDppHalfMirror>(bi));
-        argmax_step(bv, bi, dpp<kDppMirror>(bv), dpp<kDppMirror>(bi));
+        for (int j = 0; j < VPL; ++j) m[j] = key[j];
 #pragma unroll
-        for (int off = 16; off < LPT; off <<= 1)
-            argmax_step(bv, bi, __shfl_xor(bv, off, LPT), __shfl_xor(bi, off, LPT));
-        if (bi % LPT == g) taken |= 1u << (bi / LPT);
-        if (g == k) { my_logit = bv; my_id = bi; }
+        for (int w = 1; w < VPL; w <<= 1)
+#pragma unroll
+            for (int j = 0; j + w < VPL; j += 2 * w) m[j] = umax64(m[j], m[j + w]);
+        uint64_t best = m[0];
+        best = umax64(best, dpp64<kDppXor1>(best));
+        best = umax64(best, dpp64<kDppXor2>(best));
+        best = umax64(best, dpp64<kDppHalfMirror>(best));
+        best = umax64(best, dpp64<kDppMirror>(best));
+#pragma unroll
+        for (int off = 16; off < LPT; off <<= 1) best = umax64(best, shfl_xor64(best, off, LPT));
+        // the winner leaves the running: its key keeps only the low word
+        const uint32_t won = static_cast<uint32_t>(best);
+#pragma unroll
+        for (int j = 0; j < VPL; ++j)
+            if (static_cast<uint32_t>(key[j]) == won) key[j] = won;
+        if (g == k) { my_logit = key_logit(best); my_id = static_cast<int>(0xFFFFFFFFu - won); }
     }
     const double top = static_cast<double>(__shfl(my_logit, 0, LPT));
     const double ex = g < K ? exp(static_cast<double>(my_logit) - top) : 0.0;
@@ -113,34 +158,50 @@ __global__ __launch_bounds__(kTopkThreads) void route_topk_kernel(
         denom = 0.0;
         for (int k = 0; k < K; ++k) denom += __shfl(ex, k, LPT);
     }
+    const float prob = static_cast<float>(ex / denom);
+    const bool pick = live_token && g < K && static_cast<unsigned>(my_id) < static_cast<unsigned>(E);
     if (t < N && g < K) {
         topk_ids[static_cast<size_t>(t) * K + g] = live_token ? my_id : -1;
-        topk_probs[static_cast<size_t>(t) * K + g] = live_token ? static_cast<float>(ex / denom) : 0.0f;
+        topk_probs[static_cast<size_t>(t) * K + g] = live_token ? prob : 0.0f;
     }
+    if (pick) pmap[static_cast<size_t>(my_id) * Np + t] = __float_as_uint(prob);
     // the fused align counts kept routes per token with atomics: start at 0
     if (zero_count && t < N && g == 0) zero_count[t] = 0;
+    __syncthreads();                          // the piece is zeroed
+    if (pick) reinterpret_cast<uint8_t*>(s_map)[my_id * TPB + tl] = static_cast<uint8_t>(g + 1);
+    __syncthreads();
+    // expert e's TPB bytes of this block's tokens, one store each
+    const size_t col = static_cast<size_t>(blockIdx.x) * TPB;
+    for (int e = threadIdx.x; e < E; e += kTopkThreads) {
+        uint8_t* dst = map + static_cast<size_t>(e) * Np + col;
+        if (TPB == 16) *reinterpret_cast<uint4*>(dst) = reinterpret_cast<const uint4*>(s_map)[e];
+        else if (TPB == 8) *reinterpret_cast<uint2*>(dst) = reinterpret_cast<const uint2*>(s_map)[e];
+        else *reinterpret_cast<uint32_t*>(dst) = s_map[e];
+    }
 }
 
 // ---------------------------------------------------------------------------
-// capacity_select: one 1024-thread workgroup per expert.
-//  1. Compaction: scan topk_ids in route order (t*K + k, i.e. token order),
-//     per-thread match masks over 32 routes + a block prefix scan, and append
-//     this expert's candidate route indices to LDS.  If load <= C every
+// capacity_select: one workgroup per expert.
+//  1. Compaction: read the expert's rows of the routing map (one 16-byte
+//     piece of picks and its 64 bytes of probabilities per thread, in one
+//     round trip), one block prefix scan, and append one 64-bit key per
+//     candidate to LDS in token order: (probability << 32) | (2^32-1 - r),
+//     r = t*K + k the route.  Routes grow with the token, so the larger key
+//     is the one kept first -- larger probability, then the lower token --
+//     and every key is distinct and names its route.  If load <= C every
 //     candidate is kept in that order and the kernel is done.
-//  2. Else gather the candidates' probabilities (bit patterns) in one batch.
-//     Up to 2048 candidates: rank each one by counting those that beat it and
-//     keep ranks < C.  Beyond that: radix-select (4 x 8-bit digits, LDS
-//     histograms) the C-th
-//     largest probability T and how many candidates equal to T still fit.
-//     Probabilities are positive floats, so their bit patterns order like
-//     their values.
-//  3. Keep key > T, plus the first `need` candidates with key == T in token
-//     order; a second block scan numbers the kept routes 0..count-1 in token
-//     order.  Every route_slot entry of this expert gets exactly one write.
+//  2. Else up to kRankMax candidates: a sample select finds the C-th largest
+//     key T exactly.  Beyond that: radix-select (4 x 8-bit digits, LDS
+//     histograms) the C-th largest probability and how many candidates equal
+//     to it still fit.  Probabilities are positive floats, so their bit
+//     patterns order like their values.
+//  3. Keep the candidates at or above the threshold (ties in token order); a
+//     second block scan numbers the kept routes 0..count-1 in token order.
+//     Every route_slot entry of this expert gets exactly one write.
+// LDS is sized by N at launch: the keys (N) and, for the sample select, the
+// keys of its bracket (up to kRankMax).
 // ---------------------------------------------------------------------------
-constexpr int kSelThreads = 1024;
-constexpr int kSelChunk = 32;   // routes per thread per compaction pass
-constexpr int kRankMax = 2048;  // rank counting up to this load, radix select above
+constexpr int kRankMax = 2048;  // sample select up to this load, radix select above
 
 // Step 3's outputs, when the selection writes them itself (the fused
 // route + capacity + align call).  Expert e's workgroup owns its segment of
@@ -176,155 +237,230 @@ __device__ __forceinline__ void emit_route(const AlignOut& ao, int e, int r, int
 // The rest of expert e's segment once `kept` slots are taken: pad slots
 // (sentinel row N, probability +0), the blocks' owner, the first block, and
 // (expert 0) the padded extent.
-__device__ __forceinline__ void emit_segment(const AlignOut& ao, int e, int kept, int tid) {
+__device__ __forceinline__ void emit_segment(const AlignOut& ao, int e, int kept, int tid, int nthreads) {
     if (!ao.sorted_slot_ids) return;
-    for (int j = kept + tid; j < ao.Cp; j += kSelThreads) {
+    for (int j = kept + tid; j < ao.Cp; j += nthreads) {
         ao.sorted_slot_ids[e * ao.Cp + j] = ao.N;
         ao.slot_probs[e * ao.Cp + j] = 0.0f;
     }
     const int blocks = ao.Cp / kBlockM;
-    for (int b = tid; b < blocks; b += kSelThreads) ao.expert_ids[e * blocks + b] = e;
+    for (int b = tid; b < blocks; b += nthreads) ao.expert_ids[e * blocks + b] = e;
     if (tid == 0) {
         ao.block_start[e] = e * blocks;
         if (e == 0) ao.num_tokens_post_padded[0] = ao.E * ao.Cp;
     }
 }
 
-__global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
-    const int* __restrict__ ids, const float* __restrict__ probs, int NK, int C,
+// LDS of one selection workgroup, in 32-bit words: two per key for N keys
+// rounded up to 16, then two per bracket key for up to kRankMax of them.
+inline int round16(int n) { return (n + 15) & ~15; }
+inline size_t select_lds_bytes(int N) {
+    return static_cast<size_t>(2 * round16(N) + 2 * round16(std::min(N, kRankMax))) * 4u;
+}
+__device__ __forceinline__ int key_route(uint64_t key) {
+    return static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key));
+}
+__device__ __forceinline__ uint32_t key_prob(uint64_t key) { return static_cast<uint32_t>(key >> 32); }
+
+// Sum over each 16-lane row, left in every lane of the row (DPP lane moves).
+__device__ __forceinline__ int row_sum(int v) {
+    v += dpp<kDppXor1>(v);
+    v += dpp<kDppXor2>(v);
+    v += dpp<kDppHalfMirror>(v);
+    v += dpp<kDppMirror>(v);
+    return v;
+}
+// Maximum over the whole wave, uniform: DPP inside the rows, then the four
+// row maxima read as scalars.
+__device__ __forceinline__ int wave_max(int v) {
+    v = max(v, dpp<kDppXor1>(v));
+    v = max(v, dpp<kDppXor2>(v));
+    v = max(v, dpp<kDppHalfMirror>(v));
+    v = max(v, dpp<kDppMirror>(v));
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Bytes of a 16-byte map piece that hold a pick: bit j of the result for
+// byte j in 1..K (larger values are not trusted) of a token t < N.
+__device__ __forceinline__ uint32_t pick_mask(uint4 q, int t0, int N, int K) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t m = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const uint32_t b = (w[j >> 2] >> (8 * (j & 3))) & 0xFFu;
+        m |= static_cast<uint32_t>(b != 0u && b <= static_cast<uint32_t>(K) && t0 + j < N) << j;
+    }
+    return m;
+}
+
+// NT threads, one 16-byte map piece each: the launch picks the narrowest
+// width that covers the map row, since the workgroup's time is the time its
+// waves take to issue their instructions on the one CU that holds them.
+template <int NT>
+__global__ __launch_bounds__(NT) void capacity_select_kernel(
+    const uint8_t* __restrict__ map, const uint32_t* __restrict__ pmap, int Np, int N, int K, int C,
     int* __restrict__ route_slot, int* __restrict__ expert_count, AlignOut ao) {
-    __shared__ uint32_t s_route[kMaxN];
-    __shared__ __attribute__((aligned(16))) uint32_t s_key[kMaxN];
-    __shared__ int s_scan[kSelThreads / kWave];
+    extern __shared__ __attribute__((aligned(16))) uint64_t s_dyn[];
+    uint64_t* s_k64 = s_dyn;                                        // [round16(N)] candidate keys
+    uint64_t* s_b = s_dyn + ((N + 15) & ~15);                       // [round16(min(N, kRankMax))] bracket
+    constexpr int kSelThreads = NT;
+    __shared__ int s_scan[NT / kWave];
     __shared__ int s_hist[256];
     __shared__ uint32_t s_pick[2];
     const int e = blockIdx.x;
     const int tid = threadIdx.x;
 
-    // 1. compaction of this expert's route indices, in route (= token) order
-    int load = 0;
-    for (int base = 0; base < NK; base += kSelThreads * kSelChunk) {
-        const int start = base + tid * kSelChunk;
-        uint32_t mask = 0;
-        if (start + kSelChunk <= NK) {
-            const int4* p = reinterpret_cast<const int4*>(ids + start);
-            int4 v[kSelChunk / 4];
+    // 1. compaction: thread i holds piece i (tokens 16i .. 16i+15)
+    const int pieces = Np / 16;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u), pv[4];
 #pragma unroll
-            for (int q = 0; q < kSelChunk / 4; ++q) v[q] = p[q];   // all loads in flight at once
+    for (int q = 0; q < 4; ++q) pv[q] = v;
+    if (tid < pieces) {   // the piece's picks and their probabilities, in one round trip
+        v = reinterpret_cast<const uint4*>(map + static_cast<size_t>(e) * Np)[tid];
+        const uint4* prow = reinterpret_cast<const uint4*>(pmap + static_cast<size_t>(e) * Np) + 4 * tid;
 #pragma unroll
-            for (int q = 0; q < kSelChunk / 4; ++q) {
-                mask |= (v[q].x == e ? 1u : 0u) << (4 * q + 0);
-                mask |= (v[q].y == e ? 1u : 0u) << (4 * q + 1);
-                mask |= (v[q].z == e ? 1u : 0u) << (4 * q + 2);
-                mask |= (v[q].w == e ? 1u : 0u) << (4 * q + 3);
-            }
-        } else {
-            for (int j = 0; j < kSelChunk; ++j)
-                if (start + j < NK && ids[start + j] == e) mask |= 1u << j;
-        }
-        int total = 0;
-        int pos = load + block_exclusive_scan(__popc(mask), s_scan, &total);
-        while (mask) {
-            const int j = __ffs(mask) - 1;
-            mask &= mask - 1;
-            if (pos < kMaxN) s_route[pos] = static_cast<uint32_t>(start + j);   // load <= N <= kMaxN
-            ++pos;
-        }
-        load += total;
+        for (int q = 0; q < 4; ++q) pv[q] = prow[q];
     }
-    load = min(load, static_cast<int>(kMaxN));
+    const uint32_t m = pick_mask(v, tid * 16, N, K);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const uint32_t pw[16] = {pv[0].x, pv[0].y, pv[0].z, pv[0].w, pv[1].x, pv[1].y, pv[1].z, pv[1].w,
+                             pv[2].x, pv[2].y, pv[2].z, pv[2].w, pv[3].x, pv[3].y, pv[3].z, pv[3].w};
+    int load = 0;
+    int pos = block_exclusive_scan(__popc(m), s_scan, &load);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        if ((m >> j) & 1u) {
+            const int k = static_cast<int>((w[j >> 2] >> (8 * (j & 3))) & 0xFFu) - 1;
+            const uint32_t r = static_cast<uint32_t>((tid * 16 + j) * K + k);
+            s_k64[pos++] = (static_cast<uint64_t>(pw[j]) << 32) | (0xFFFFFFFFu - r);
+        }
+    }
+    // zero keys past `load` up to a multiple of 16: below every candidate's
+    // (whose low word is never 0), so a zero key never counts
+    const int padded = (load + 15) & ~15;
+    if (tid < padded - load) s_k64[load + tid] = 0ull;
     __syncthreads();
 
     if (load <= C) {   // every candidate fits: slot = position in token order
         for (int i = tid; i < load; i += kSelThreads) {
-            const int r = static_cast<int>(s_route[i]);
-            route_slot[r] = i;
-            if (ao.sorted_slot_ids) emit_route(ao, e, r, i, probs[r]);
+            const uint64_t k = s_k64[i];
+            route_slot[key_route(k)] = i;
+            emit_route(ao, e, key_route(k), i, __uint_as_float(key_prob(k)));
         }
-        emit_segment(ao, e, load, tid);
+        emit_segment(ao, e, load, tid, NT);
         if (tid == 0) expert_count[e] = load;
         return;
     }
-    // over capacity: gather the candidates' probabilities (one batch of loads);
-    // keys past `load` up to a multiple of 16 are zero (a zero key never beats
-    // a probability, which is > 0)
-    const int padded = (load + 15) & ~15;
-    for (int i = tid; i < padded; i += kSelThreads)
-        s_key[i] = i < load ? __float_as_uint(probs[s_route[i]]) : 0u;
-    __syncthreads();
 
     if (load <= kRankMax) {
-        // 2'. rank counting: candidate i is kept iff fewer than C candidates
-        // beat it (a larger key, or an equal key and a lower token, which in
-        // this token-ordered list means a lower position).  Both rules fold
-        // into one 64-bit key, (key << 32) | (2^32 - 1 - position): j beats i
-        // iff its 64-bit key is larger.  Wave w counts, for the 64 candidates
-        // of group w % G, the beaters among the P-th part w / G of the list
-        // (G groups, P = waves / G parts), and the parts add up in LDS.  All
-        // lanes of a wave read the same key at once (an LDS broadcast), so
-        // there is no contention, unlike histogram atomics on the few exponent
-        // digits the probabilities share.  Ranks live past the keys
-        // (s_key[kRankMax..]), the 64-bit keys past those; kept flags go to
-        // bit 31 of s_route.  Keys past `load` are zero and never beat a
-        // probability, which is > 0.
-        uint32_t* s_rank = s_key + kRankMax;
-        uint64_t* s_k64 = reinterpret_cast<uint64_t*>(s_key + 2 * kRankMax);
-        for (int i = tid; i < padded; i += kSelThreads) {
-            if (i < load) s_rank[i] = 0;
-            s_k64[i] = i < load ? (static_cast<uint64_t>(s_key[i]) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(i))
-                                : 0ull;
-        }
-        __syncthreads();
-        constexpr int kWaves = kSelThreads / kWave;
-        const int groups = (load + kWave - 1) / kWave;             // waves take turns when > kWaves
-        const int wave = tid / kWave, lane = tid % kWave;
-        for (int task = wave; task < groups * max(1, kWaves / groups); task += kWaves) {
-            const int parts = max(1, kWaves / groups);
-            const int g = task % groups, part = task / groups;
-            const int chunk = (padded / 16 + parts - 1) / parts * 16;   // keys per part
-            const int j0 = part * chunk, j1 = min(padded, j0 + chunk);
-            const int i = g * kWave + lane;
-            const uint64_t ki = i < load ? s_k64[i] : ~0ull;
-            int rank = 0;
-            const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(s_k64);
-            for (int j = j0; j < j1; j += 16) {   // 8 independent 16-byte reads per trip
-                ulonglong2 q[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) q[u] = k2[j / 2 + u];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) rank += (q[u].x > ki) + (q[u].y > ki);
+        // 2'. sample select of T, the C-th largest key; the kept candidates
+        // are exactly those with key >= T.
+        //  a. NT/16 splitters (the candidates at positions s*load/S) are ranked
+        //     against every key: the 16 lanes of a splitter's row count every
+        //     16th key each and add up across the row;
+        //  b. hi = the splitter of largest rank <= C-1 (key >= T) and lo = the
+        //     one of smallest rank >= C (key < T) bracket T;
+        //  c. unless hi is T itself, T is the key strictly inside the bracket
+        //     whose rank, hi's rank + 1 + the bracket keys above it, is C-1.
+        // The work is one pass over the keys plus the bracket (about load/S
+        // keys) squared, instead of every pair of candidates.
+        constexpr int S = NT / 16;                                 // splitters (<= 64)
+        __shared__ uint64_t s_spl_key[S];
+        __shared__ int s_spl_rank[S];
+        __shared__ uint64_t s_bracket[3];                          // lo, hi, T
+        __shared__ int s_rank_hi, s_bn;
+        {
+            const int sp = tid / 16, part = tid % 16;
+            const uint64_t ks = s_k64[sp * load / S];
+            int cnt = 0;
+#pragma unroll 4
+            for (int j = part; j < padded; j += 16) cnt += s_k64[j] > ks;
+            cnt = row_sum(cnt);                                    // the splitter's rank, in its whole row
+            if (part == 0) {
+                s_spl_key[sp] = ks;
+                s_spl_rank[sp] = cnt;
             }
-            if (i < load && rank) atomicAdd(&s_rank[i], static_cast<uint32_t>(rank));
         }
         __syncthreads();
-        for (int i = tid; i < load; i += kSelThreads)
-            if (s_rank[i] < static_cast<uint32_t>(C)) s_route[i] |= 0x80000000u;
+        if (tid < kWave) {
+            // lane q < S holds splitter q
+            const bool real = tid < S;
+            const int r = real ? s_spl_rank[tid] : -1;
+            const uint64_t kq = real ? s_spl_key[tid] : 0ull;
+            const int rhi = wave_max(real && r <= C - 1 ? r : -1);          // -1: no splitter at or above T
+            const int rlo = -wave_max(real && r >= C ? -r : -INT32_MAX);     // INT32_MAX: none below T
+            if (tid == 0) {
+                s_bracket[0] = 0ull;                               // open ends: below and above every key
+                s_bracket[1] = ~0ull;
+                s_bracket[2] = ~0ull;                              // T, unless found below (C = 0: none kept)
+                s_rank_hi = rhi;
+                s_bn = 0;
+            }
+            // the splitters of those ranks name the bracket (repeated
+            // splitters write the same key); a splitter of rank C-1 is T
+            if (real && r == rlo) s_bracket[0] = kq;
+            if (real && r == rhi) s_bracket[1] = kq;
+            if (real && r == rhi && rhi == C - 1) s_bracket[2] = kq;
+        }
         __syncthreads();
+        const uint64_t klo = s_bracket[0], khi = s_bracket[1];
+        const bool search = C > 0 && s_rank_hi != C - 1;          // uniform
+        if (search) {
+            for (int i = tid; i < load; i += kSelThreads) {
+                const uint64_t k = s_k64[i];
+                if (k > klo && k < khi) s_b[atomicAdd(&s_bn, 1)] = k;   // order within the bracket is free
+            }
+        }
+        __syncthreads();
+        // zero past the bracket's keys to a multiple of 8 (room: nb <= load <= kRankMax)
+        const int nb = search ? s_bn : 0;
+        const int nb8 = (nb + 7) & ~7;
+        if (tid < nb8 - nb) s_b[nb + tid] = 0ull;
+        __syncthreads();
+        if (search) {
+            for (int i = tid; i < nb; i += kSelThreads) {
+                const uint64_t k = s_b[i];
+                int r = s_rank_hi + 1;
+                for (int j = 0; j < nb8; j += 8) {   // 8 reads in flight, then the comparisons
+                    uint64_t q[8];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) q[u] = s_b[j + u];
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) r += q[u] > k;
+                }
+                if (r == C - 1) s_bracket[2] = k;                  // exactly one key has rank C-1
+            }
+        }
+        __syncthreads();
+        const uint64_t T = s_bracket[2];
+        // 3'. keep key >= T and number the kept routes in token order
         const int per = (load + kSelThreads - 1) / kSelThreads;
         const int lo = min(load, tid * per), hi = min(load, lo + per);
         int kept = 0;
-        for (int i = lo; i < hi; ++i) kept += static_cast<int>(s_route[i] >> 31);
+        for (int i = lo; i < hi; ++i) kept += s_k64[i] >= T;
         int tot = 0;
         int slot = block_exclusive_scan(kept, s_scan, &tot);
         for (int i = lo; i < hi; ++i) {
-            const uint32_t r = s_route[i];
-            const int sl = (r >> 31) ? slot++ : -1;
-            route_slot[r & 0x7FFFFFFFu] = sl;
-            emit_route(ao, e, static_cast<int>(r & 0x7FFFFFFFu), sl, __uint_as_float(s_key[i]));
+            const uint64_t k = s_k64[i];
+            const int sl = k >= T && slot < C ? slot++ : -1;
+            route_slot[key_route(k)] = sl;
+            emit_route(ao, e, key_route(k), sl, __uint_as_float(key_prob(k)));
         }
-        emit_segment(ao, e, C, tid);
-        if (tid == 0) expert_count[e] = C;
+        tot = min(tot, max(C, 0));
+        emit_segment(ao, e, tot, tid, NT);
+        if (tid == 0) expert_count[e] = tot;
         return;
     }
 
-    // 2. radix select of the C-th largest key
+    // 2. radix select of the C-th largest probability
     uint32_t prefix = 0, prefix_mask = 0;
     int remaining = C;   // rank still to locate among keys that match prefix
     for (int shift = 24; shift >= 0; shift -= 8) {
         for (int i = tid; i < 256; i += kSelThreads) s_hist[i] = 0;
         __syncthreads();
         for (int i = tid; i < load; i += kSelThreads) {
-            const uint32_t k = s_key[i];
+            const uint32_t k = key_prob(s_k64[i]);
             if ((k & prefix_mask) == prefix) atomicAdd(&s_hist[(k >> shift) & 255u], 1);
         }
         __syncthreads();
@@ -355,14 +491,14 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
         __syncthreads();
     }
     const uint32_t T = prefix;
-    const int need = remaining;   // candidates with key == T that are kept
+    const int need = remaining;   // candidates with probability == T that are kept
 
     // 3. keep and number in token order (contiguous chunks keep the order)
     const int per = (load + kSelThreads - 1) / kSelThreads;
     const int lo = min(load, tid * per), hi = min(load, lo + per);
     int gt = 0, eq = 0;
     for (int i = lo; i < hi; ++i) {
-        const uint32_t k = s_key[i];
+        const uint32_t k = key_prob(s_k64[i]);
         gt += k > T;
         eq += k == T;
     }
@@ -372,42 +508,77 @@ __global__ __launch_bounds__(kSelThreads) void capacity_select_kernel(
     int slot = block_exclusive_scan(gt + eq_keep, s_scan, &tot);
     int eq_seen = eq_base;
     for (int i = lo; i < hi; ++i) {
-        const uint32_t k = s_key[i];
+        const uint64_t key = s_k64[i];
+        const uint32_t k = key_prob(key);
         bool keep = k > T;
         if (k == T) { keep = eq_seen < need; ++eq_seen; }
         const int sl = keep ? slot++ : -1;
-        route_slot[s_route[i]] = sl;
-        emit_route(ao, e, static_cast<int>(s_route[i]), sl, __uint_as_float(k));
+        route_slot[key_route(key)] = sl;
+        emit_route(ao, e, key_route(key), sl, __uint_as_float(k));
     }
-    emit_segment(ao, e, C, tid);
+    emit_segment(ao, e, C, tid, NT);
     if (tid == 0) expert_count[e] = C;
 }
 
+// The routing map in the workspace: the pick bytes ([E, Np], Np = N rounded
+// up to 16), then the pick probabilities ([E, Np] words).
+struct RouteMap {
+    uint8_t* picks;
+    uint32_t* probs;
+    int Np;
+};
+
 template <int LPT, int VPL>
 void launch_topk(const float* logits, int N, int E, int K, int* ids, float* probs, int* zero_count,
-                 const int* n_live, hipStream_t s) {
+                 const int* n_live, const RouteMap& rm, hipStream_t s) {
     constexpr int TPB = kTopkThreads / LPT;
-    const int blocks = (N + TPB - 1) / TPB;
+    const int blocks = rm.Np / TPB;               // every byte of the map's rows, tail included
     route_topk_kernel<LPT, VPL><<<blocks, kTopkThreads, 0, s>>>(logits, N, E, K, ids, probs, zero_count,
-                                                                n_live);
+                                                                n_live, rm.picks, rm.probs, rm.Np);
 }
 
 // Lanes per token: enough for K (lane k finishes route k) and for E in at
 // most 8 logits per lane when it fits, else all 64 lanes.
 void dispatch_topk(const float* logits, int N, int E, int K, int* ids, float* probs, int* zero_count,
-                   hipStream_t s, const int* n_live = nullptr) {
+                   const RouteMap& rm, hipStream_t s, const int* n_live = nullptr) {
     if (K <= 16 && E <= 128) {
-        if (E <= 32) launch_topk<16, 2>(logits, N, E, K, ids, probs, zero_count, n_live, s);
-        else if (E <= 64) launch_topk<16, 4>(logits, N, E, K, ids, probs, zero_count, n_live, s);
-        else launch_topk<16, 8>(logits, N, E, K, ids, probs, zero_count, n_live, s);
+        if (E <= 32) launch_topk<16, 2>(logits, N, E, K, ids, probs, zero_count, n_live, rm, s);
+        else if (E <= 64) launch_topk<16, 4>(logits, N, E, K, ids, probs, zero_count, n_live, rm, s);
+        else launch_topk<16, 8>(logits, N, E, K, ids, probs, zero_count, n_live, rm, s);
     } else if (E <= 256) {
-        if (E <= 128) launch_topk<32, 4>(logits, N, E, K, ids, probs, zero_count, n_live, s);
-        else launch_topk<32, 8>(logits, N, E, K, ids, probs, zero_count, n_live, s);
+        if (E <= 128) launch_topk<32, 4>(logits, N, E, K, ids, probs, zero_count, n_live, rm, s);
+        else launch_topk<32, 8>(logits, N, E, K, ids, probs, zero_count, n_live, rm, s);
     } else if (E <= 512) {
-        launch_topk<64, 8>(logits, N, E, K, ids, probs, zero_count, n_live, s);
+        launch_topk<64, 8>(logits, N, E, K, ids, probs, zero_count, n_live, rm, s);
     } else {
-        launch_topk<64, 16>(logits, N, E, K, ids, probs, zero_count, n_live, s);
+        launch_topk<64, 16>(logits, N, E, K, ids, probs, zero_count, n_live, rm, s);
     }
+}
+
+template <int T>
+void launch_select_t(const RouteMap& rm, int N, int E, int K, int C, int* route_slot,
+                     int* expert_count, const AlignOut& ao, hipStream_t s) {
+    const size_t lds = select_lds_bytes(N);
+    static std::atomic<bool> raised{false};
+    if (lds > 64 * 1024 && !raised.load(std::memory_order_relaxed)) {
+        // past 64 KB of dynamic LDS the launch needs the kernel's limit raised
+        (void)hipFuncSetAttribute(reinterpret_cast<const void*>(capacity_select_kernel<T>),
+                                  hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  static_cast<int>(select_lds_bytes(static_cast<int>(kMaxN))));
+        raised.store(true, std::memory_order_relaxed);
+    }
+    capacity_select_kernel<T><<<E, T, lds, s>>>(rm.picks, rm.probs, rm.Np, N, K, C, route_slot,
+                                                expert_count, ao);
+}
+
+// One map piece (16 tokens) per thread: the narrowest width that covers N.
+void launch_select(const RouteMap& rm, int N, int E, int K, int C, int* route_slot,
+                   int* expert_count, const AlignOut& ao, hipStream_t s) {
+    static_assert(kMaxN <= 16 * 1024, "one map piece per thread");
+    const int pieces = rm.Np / 16;
+    if (pieces <= 256) launch_select_t<256>(rm, N, E, K, C, route_slot, expert_count, ao, s);
+    else if (pieces <= 512) launch_select_t<512>(rm, N, E, K, C, route_slot, expert_count, ao, s);
+    else launch_select_t<1024>(rm, N, E, K, C, route_slot, expert_count, ao, s);
 }
 
 }  // namespace
@@ -424,61 +595,45 @@ int check_route_ptrs(std::initializer_list<const void*> ptrs) {
     return MOE_OK;
 }
 
-}  // namespace
-}  // namespace moe
+// Row pitch of the routing map: N rounded up to whole 16-byte pieces.
+int64_t map_pitch(int64_t N) { return (N + 15) / 16 * 16; }
 
-extern "C" int moe_route_capacity(const float* logits, int64_t N, int32_t E, int32_t K, int64_t C,
-                                  int32_t* topk_ids, float* topk_probs, int32_t* route_slot,
-                                  int32_t* expert_count, hipStream_t stream) {
-    using namespace moe;
-    int st = check_route_shape(N, E, K, C);
-    if (st != MOE_OK) return st;
-    if (N == 0) return MOE_OK;
-    st = check_route_ptrs({logits, topk_ids, topk_probs, route_slot, expert_count});
-    if (st != MOE_OK) return st;
-    const int n = static_cast<int>(N);
-    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, nullptr, stream);
-    capacity_select_kernel<<<E, kSelThreads, 0, stream>>>(topk_ids, topk_probs, n * K,
-                                                          static_cast<int>(C), route_slot,
-                                                          expert_count, AlignOut{});
-    return launch_status();
+// Workspace bytes: the pick bytes and the pick probabilities, E rows each.
+size_t map_bytes(int64_t N, int32_t E) {
+    return static_cast<size_t>(E) * static_cast<size_t>(map_pitch(N)) * 5u;
 }
 
-extern "C" int moe_route_capacity_align(const float* logits, int64_t N, int32_t E, int32_t K,
-                                        int64_t C, int32_t* topk_ids, float* topk_probs,
-                                        int32_t* route_slot, int32_t* expert_count,
-                                        int32_t* sorted_slot_ids, float* slot_probs,
-                                        int32_t* expert_ids, int32_t* block_start,
-                                        int32_t* token_routes, int32_t* token_route_count,
-                                        int32_t* num_tokens_post_padded, hipStream_t stream) {
-    using namespace moe;
-    int st = check_route_shape(N, E, K, C);
-    if (st != MOE_OK) return st;
-    if (N == 0) return MOE_OK;
-    st = check_route_ptrs({logits, topk_ids, topk_probs, route_slot, expert_count, sorted_slot_ids,
-                           slot_probs, expert_ids, block_start, token_routes, token_route_count,
-                           num_tokens_post_padded});
-    if (st != MOE_OK) return st;
-    const int n = static_cast<int>(N);
-    const AlignOut ao{sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
-                      token_route_count, num_tokens_post_padded, n, K, E,
-                      static_cast<int>(moe_padded_capacity(C))};
-    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, token_route_count, stream);
-    capacity_select_kernel<<<E, kSelThreads, 0, stream>>>(topk_ids, topk_probs, n * K,
-                                                          static_cast<int>(C), route_slot,
-                                                          expert_count, ao);
-    return launch_status();
+RouteMap route_map(void* ws, int64_t N, int32_t E) {
+    const int64_t Np = map_pitch(N);
+    uint8_t* picks = static_cast<uint8_t*>(ws);
+    return RouteMap{picks, reinterpret_cast<uint32_t*>(picks + static_cast<size_t>(E) * Np),
+                    static_cast<int>(Np)};
 }
 
-namespace moe {
-namespace {
+// The routing map lives in the caller's workspace: present, aligned, large enough.
+int check_workspace(const void* ws, size_t bytes, int64_t N, int32_t E) {
+    if (!ws) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(ws)) return MOE_ERR_MISALIGNED;
+    if (bytes < map_bytes(N, E)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+// Steps 1-2 (align outputs in `ao` when the call also does step 3), once the
+// arguments are validated; the routing map goes to the workspace.
+void route_capacity_launch(const float* logits, int n, int E, int K, int C, int32_t* topk_ids,
+                           float* topk_probs, int32_t* route_slot, int32_t* expert_count,
+                           const AlignOut& ao, void* workspace, hipStream_t stream) {
+    const RouteMap rm = route_map(workspace, n, E);
+    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, ao.token_route_count, rm, stream);
+    launch_select(rm, n, E, K, C, route_slot, expert_count, ao, stream);
+}
 
 int route_dropless(const float* logits, int64_t N, int32_t E, int32_t K, const int32_t* n_live,
                    int32_t* topk_ids, float* topk_probs, int32_t* route_within,
                    int32_t* route_counts, int32_t* sorted_slot_ids, float* slot_probs,
                    int32_t* expert_ids, int32_t* block_start, int32_t* token_routes,
-                   int32_t* token_route_count, int32_t* num_tokens_post_padded,
-                   hipStream_t stream) {
+                   int32_t* token_route_count, int32_t* num_tokens_post_padded, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
     int st = check_route_shape(N, E, K, N);
     if (st != MOE_OK) return st;
     if (moe_dropless_bound(N, K, E) > INT32_MAX) return MOE_ERR_UNSUPPORTED;
@@ -487,14 +642,15 @@ int route_dropless(const float* logits, int64_t N, int32_t E, int32_t K, const i
                            sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
                            token_route_count, num_tokens_post_padded});
     if (st != MOE_OK) return st;
+    st = check_workspace(workspace, workspace_bytes, N, E);
+    if (st != MOE_OK) return st;
     const int n = static_cast<int>(N);
-    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, nullptr, stream, n_live);
+    const RouteMap rm = route_map(workspace, N, E);
+    dispatch_topk(logits, n, E, K, topk_ids, topk_probs, nullptr, rm, stream, n_live);
     // A capacity of N never binds (an expert gets at most one route per
     // token): the selection pass then only ranks each expert's routes in
-    // token order and counts them.  Routes of tokens past n_live carry
-    // expert -1 and match no expert.
-    capacity_select_kernel<<<E, kSelThreads, 0, stream>>>(topk_ids, topk_probs, n * K, n,
-                                                          route_within, route_counts, AlignOut{});
+    // token order and counts them.  Tokens past n_live have no picks in the map.
+    launch_select(rm, n, E, K, n, route_within, route_counts, AlignOut{}, stream);
     st = launch_align_dropless(topk_ids, topk_probs, route_within, route_counts, N, E, K,
                                sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
                                token_route_count, num_tokens_post_padded, stream, n_live);
@@ -504,15 +660,67 @@ int route_dropless(const float* logits, int64_t N, int32_t E, int32_t K, const i
 }  // namespace
 }  // namespace moe
 
+extern "C" size_t moe_route_capacity_workspace_bytes(int64_t N, int32_t E, int32_t K) {
+    if (N < 0 || E < 1 || K < 1 || K > E || N > moe::kMaxN || E > moe::kMaxE || K > moe::kMaxK)
+        return 0;
+    return moe::map_bytes(N, E);
+}
+
+extern "C" int moe_route_capacity(const float* logits, int64_t N, int32_t E, int32_t K, int64_t C,
+                                  int32_t* topk_ids, float* topk_probs, int32_t* route_slot,
+                                  int32_t* expert_count, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+    using namespace moe;
+    int st = check_route_shape(N, E, K, C);
+    if (st != MOE_OK) return st;
+    if (N == 0) return MOE_OK;
+    st = check_route_ptrs({logits, topk_ids, topk_probs, route_slot, expert_count});
+    if (st != MOE_OK) return st;
+    st = check_workspace(workspace, workspace_bytes, N, E);
+    if (st != MOE_OK) return st;
+    route_capacity_launch(logits, static_cast<int>(N), E, K, static_cast<int>(C), topk_ids,
+                          topk_probs, route_slot, expert_count, AlignOut{}, workspace, stream);
+    return launch_status();
+}
+
+extern "C" int moe_route_capacity_align(const float* logits, int64_t N, int32_t E, int32_t K,
+                                        int64_t C, int32_t* topk_ids, float* topk_probs,
+                                        int32_t* route_slot, int32_t* expert_count,
+                                        int32_t* sorted_slot_ids, float* slot_probs,
+                                        int32_t* expert_ids, int32_t* block_start,
+                                        int32_t* token_routes, int32_t* token_route_count,
+                                        int32_t* num_tokens_post_padded, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream) {
+    using namespace moe;
+    int st = check_route_shape(N, E, K, C);
+    if (st != MOE_OK) return st;
+    if (N == 0) return MOE_OK;
+    st = check_route_ptrs({logits, topk_ids, topk_probs, route_slot, expert_count, sorted_slot_ids,
+                           slot_probs, expert_ids, block_start, token_routes, token_route_count,
+                           num_tokens_post_padded});
+    if (st != MOE_OK) return st;
+    st = check_workspace(workspace, workspace_bytes, N, E);
+    if (st != MOE_OK) return st;
+    const int n = static_cast<int>(N);
+    const AlignOut ao{sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
+                      token_route_count, num_tokens_post_padded, n, K, E,
+                      static_cast<int>(moe_padded_capacity(C))};
+    route_capacity_launch(logits, n, E, K, static_cast<int>(C), topk_ids, topk_probs, route_slot,
+                          expert_count, ao, workspace, stream);
+    return launch_status();
+}
+
 extern "C" int moe_route_dropless(const float* logits, int64_t N, int32_t E, int32_t K,
                                   int32_t* topk_ids, float* topk_probs, int32_t* route_within,
                                   int32_t* route_counts, int32_t* sorted_slot_ids,
                                   float* slot_probs, int32_t* expert_ids, int32_t* block_start,
                                   int32_t* token_routes, int32_t* token_route_count,
-                                  int32_t* num_tokens_post_padded, hipStream_t stream) {
+                                  int32_t* num_tokens_post_padded, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
     return moe::route_dropless(logits, N, E, K, nullptr, topk_ids, topk_probs, route_within,
                                route_counts, sorted_slot_ids, slot_probs, expert_ids, block_start,
-                               token_routes, token_route_count, num_tokens_post_padded, stream);
+                               token_routes, token_route_count, num_tokens_post_padded, workspace,
+                               workspace_bytes, stream);
 }
 
 extern "C" int moe_route_dropless_live(const float* logits, int64_t N, int32_t E, int32_t K,
@@ -522,10 +730,12 @@ extern "C" int moe_route_dropless_live(const float* logits, int64_t N, int32_t E
                                        float* slot_probs, int32_t* expert_ids,
                                        int32_t* block_start, int32_t* token_routes,
                                        int32_t* token_route_count,
-                                       int32_t* num_tokens_post_padded, hipStream_t stream) {
+                                       int32_t* num_tokens_post_padded, void* workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
     if (!n_live) return MOE_ERR_INVALID_ARG;
     if (!moe::aligned16(n_live)) return MOE_ERR_MISALIGNED;
     return moe::route_dropless(logits, N, E, K, n_live, topk_ids, topk_probs, route_within,
                                route_counts, sorted_slot_ids, slot_probs, expert_ids, block_start,
-                               token_routes, token_route_count, num_tokens_post_padded, stream);
+                               token_routes, token_route_count, num_tokens_post_padded, workspace,
+                               workspace_bytes, stream);
 }

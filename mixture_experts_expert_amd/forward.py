@@ -43,10 +43,11 @@ class MoEBuffers:
         self.act = z((self.R, I), bf16)
         self.route_out = z((self.R, H), bf16)
         self.y = z((N, H), bf16)
+        self.workspace = nat.route_workspace(N, E, K, dev)   # the routing map
 
     def route_capacity(self, logits, stream=None):
         nat.moe_route_capacity(logits, self.K, self.C, self.topk_ids, self.topk_probs,
-                               self.route_slot, self.expert_count, stream)
+                               self.route_slot, self.expert_count, self.workspace, stream)
 
     def route_capacity_align(self, logits, stream=None):
         """Steps 1-3 in two launches (the selection writes the route list)."""
@@ -54,7 +55,7 @@ class MoEBuffers:
                                      self.route_slot, self.expert_count, self.sorted_slot_ids,
                                      self.slot_probs, self.expert_ids, self.block_start,
                                      self.token_routes, self.token_route_count,
-                                     self.num_tokens_post_padded, stream)
+                                     self.num_tokens_post_padded, self.workspace, stream)
 
     def align(self, stream=None):
         nat.moe_align(self.topk_ids, self.topk_probs, self.route_slot, self.expert_count,
@@ -196,12 +197,14 @@ class DroplessBuffers:
         self.act = z((self.R, I), bf16)
         self.route_out = z((self.R, H), bf16)
         self.y = z((N, H), bf16)
+        self.workspace = nat.route_workspace(N, E, K, dev)   # the routing map
 
     def route(self, logits, stream=None):
         nat.moe_route_dropless(logits, self.K, self.topk_ids, self.topk_probs, self.route_within,
                                self.route_counts, self.sorted_slot_ids, self.slot_probs,
                                self.expert_ids, self.block_start, self.token_routes,
-                               self.token_route_count, self.num_tokens_post_padded, stream)
+                               self.token_route_count, self.num_tokens_post_padded,
+                               self.workspace, stream)
 
     def grouped_ffn(self, x, w1, w2, stream=None):
         nat.moe_grouped_ffn_fwd_dropless(x, w1, w2, self.sorted_slot_ids, self.slot_probs,

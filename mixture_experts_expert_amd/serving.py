@@ -109,12 +109,12 @@ class ServingLadder:
                                         b.route_within[:n], b.route_counts, b.sorted_slot_ids,
                                         b.slot_probs, b.expert_ids, b.block_start,
                                         b.token_routes[:n], b.token_route_count[:n],
-                                        b.num_tokens_post_padded)
+                                        b.num_tokens_post_padded, b.workspace)
         else:
             nat.moe_route_dropless(lg, K, b.topk_ids[:n], b.topk_probs[:n], b.route_within[:n],
                                    b.route_counts, b.sorted_slot_ids, b.slot_probs, b.expert_ids,
                                    b.block_start, b.token_routes[:n], b.token_route_count[:n],
-                                   b.num_tokens_post_padded)
+                                   b.num_tokens_post_padded, b.workspace)
         nat.moe_grouped_ffn_fwd_dropless(self.x[:n], self.w1, self.w2, b.sorted_slot_ids,
                                          b.slot_probs, b.block_start, b.num_tokens_post_padded,
                                          K, b.act, b.route_out)

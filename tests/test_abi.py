@@ -27,7 +27,7 @@ def test_every_declared_symbol_is_exported():
                           "moe_grouped_fc2_dgrad", "moe_swiglu_bwd", "moe_grouped_fc1_dgrad",
                           "moe_grouped_fc2_wgrad", "moe_grouped_fc1_wgrad", "moe_route_bwd",
                           "moe_route_dropless_live", "moe_dispatch_rows",
-                          "moe_grouped_fc2_rows"}
+                          "moe_grouped_fc2_rows", "moe_route_capacity_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -77,26 +77,47 @@ ALIGNED = P(0x10000)        # never dereferenced: rejected or no-op before any l
 MIS = P(0x10004)
 
 
+WSB = ctypes.c_size_t(1 << 30)   # a workspace size that always suffices
+WS = (ALIGNED, WSB)
+
+
+def test_route_workspace_bytes():
+    f = lib.moe_route_capacity_workspace_bytes
+    for N, E, K in [(64, 4, 2), (1024, 8, 2), (4096, 128, 8), (8192, 256, 8), (1, 1, 1),
+                    (17, 3, 2), (16384, 1024, 32), (0, 4, 2)]:
+        assert f(N, E, K) == 5 * E * (-(-N // 16) * 16), (N, E, K)
+        assert moe.moe_route_capacity_workspace_bytes(N, E, K) == 5 * E * (-(-N // 16) * 16)
+    for bad in [(16, 4, 5), (16, 4, 0), (-1, 4, 2), (20000, 8, 2), (16, 2048, 8), (16, 64, 33)]:
+        assert f(*bad) == 0, bad
+
+
 def test_route_capacity_validation():
     f = lib.moe_route_capacity
-    assert f(ALIGNED, 16, 4, 5, 20, ALIGNED, ALIGNED, ALIGNED, ALIGNED, NUL) == INVALID     # K > E
-    assert f(ALIGNED, 16, 4, 0, 8, ALIGNED, ALIGNED, ALIGNED, ALIGNED, NUL) == INVALID      # K < 1
-    assert f(ALIGNED, 16, 2048, 8, 64, ALIGNED, ALIGNED, ALIGNED, ALIGNED, NUL) == UNSUPPORTED  # E
-    assert f(ALIGNED, 16, 64, 33, 64, ALIGNED, ALIGNED, ALIGNED, ALIGNED, NUL) == UNSUPPORTED   # K
-    assert f(ALIGNED, 20000, 8, 2, 5000, ALIGNED, ALIGNED, ALIGNED, ALIGNED, NUL) == UNSUPPORTED  # N
-    assert f(NUL, 16, 4, 2, 8, ALIGNED, ALIGNED, ALIGNED, ALIGNED, NUL) == INVALID
-    assert f(MIS, 16, 4, 2, 8, ALIGNED, ALIGNED, ALIGNED, ALIGNED, NUL) == MISALIGNED
-    assert f(NUL, 0, 4, 2, 0, NUL, NUL, NUL, NUL, NUL) == OK                                  # N = 0
+    a = [ALIGNED] * 4
+    assert f(ALIGNED, 16, 4, 5, 20, *a, *WS, NUL) == INVALID                 # K > E
+    assert f(ALIGNED, 16, 4, 0, 8, *a, *WS, NUL) == INVALID                  # K < 1
+    assert f(ALIGNED, 16, 2048, 8, 64, *a, *WS, NUL) == UNSUPPORTED          # E
+    assert f(ALIGNED, 16, 64, 33, 64, *a, *WS, NUL) == UNSUPPORTED           # K
+    assert f(ALIGNED, 20000, 8, 2, 5000, *a, *WS, NUL) == UNSUPPORTED        # N
+    assert f(NUL, 16, 4, 2, 8, *a, *WS, NUL) == INVALID
+    assert f(MIS, 16, 4, 2, 8, *a, *WS, NUL) == MISALIGNED
+    assert f(ALIGNED, 16, 4, 2, 8, *a, NUL, WSB, NUL) == INVALID             # no workspace
+    assert f(ALIGNED, 16, 4, 2, 8, *a, MIS, WSB, NUL) == MISALIGNED
+    # the workspace must hold 5 bytes per expert and token, tokens rounded up
+    # to 16: 5 * 4 * 32 here
+    assert f(ALIGNED, 17, 4, 2, 9, *a, ALIGNED, ctypes.c_size_t(639), NUL) == INVALID
+    assert f(NUL, 0, 4, 2, 0, NUL, NUL, NUL, NUL, NUL, ctypes.c_size_t(0), NUL) == OK   # N = 0
 
 
 def test_route_capacity_align_validation():
     f = lib.moe_route_capacity_align
     o = [ALIGNED] * 7
-    assert f(ALIGNED, 16, 4, 5, 20, *([ALIGNED] * 4), *o, NUL) == INVALID                   # K > E
-    assert f(ALIGNED, 16, 2048, 8, 64, *([ALIGNED] * 4), *o, NUL) == UNSUPPORTED            # E
-    assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o[:6], MIS, NUL) == MISALIGNED
-    assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o[:2], NUL, *o[3:], NUL) == INVALID
-    assert f(NUL, 0, 4, 2, 0, *([NUL] * 4), *([NUL] * 7), NUL) == OK                         # N = 0
+    assert f(ALIGNED, 16, 4, 5, 20, *([ALIGNED] * 4), *o, *WS, NUL) == INVALID          # K > E
+    assert f(ALIGNED, 16, 2048, 8, 64, *([ALIGNED] * 4), *o, *WS, NUL) == UNSUPPORTED   # E
+    assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o[:6], MIS, *WS, NUL) == MISALIGNED
+    assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o[:2], NUL, *o[3:], *WS, NUL) == INVALID
+    assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o, ALIGNED, ctypes.c_size_t(319), NUL) == INVALID
+    assert f(NUL, 0, 4, 2, 0, *([NUL] * 4), *([NUL] * 7), NUL, ctypes.c_size_t(0), NUL) == OK   # N = 0
 
 
 def test_dropless_bound_and_validation():
@@ -106,14 +127,16 @@ def test_dropless_bound_and_validation():
     assert lib.moe_dropless_bound(4, 5, 4) == INVALID and lib.moe_dropless_bound(20000, 2, 8) == UNSUPPORTED
     f = lib.moe_route_dropless
     o = [ALIGNED] * 11
-    assert f(ALIGNED, 16, 4, 5, *o, NUL) == INVALID                          # K > E
-    assert f(ALIGNED, 16, 4, 2, *o[:10], MIS, NUL) == MISALIGNED
-    assert f(ALIGNED, 16, 4, 2, *o[:3], NUL, *o[4:], NUL) == INVALID
-    assert f(NUL, 0, 4, 2, *([NUL] * 11), NUL) == OK                          # N = 0
+    assert f(ALIGNED, 16, 4, 5, *o, *WS, NUL) == INVALID                      # K > E
+    assert f(ALIGNED, 16, 4, 2, *o[:10], MIS, *WS, NUL) == MISALIGNED
+    assert f(ALIGNED, 16, 4, 2, *o[:3], NUL, *o[4:], *WS, NUL) == INVALID
+    assert f(ALIGNED, 16, 4, 2, *o, NUL, WSB, NUL) == INVALID                # no workspace
+    assert f(NUL, 0, 4, 2, *([NUL] * 11), NUL, ctypes.c_size_t(0), NUL) == OK  # N = 0
     v = lib.moe_route_dropless_live
-    assert v(ALIGNED, 16, 4, 2, NUL, *o, NUL) == INVALID                      # no live count
-    assert v(ALIGNED, 16, 4, 2, MIS, *o, NUL) == MISALIGNED
-    assert v(ALIGNED, 16, 4, 5, ALIGNED, *o, NUL) == INVALID                  # K > E
+    assert v(ALIGNED, 16, 4, 2, NUL, *o, *WS, NUL) == INVALID                  # no live count
+    assert v(ALIGNED, 16, 4, 2, MIS, *o, *WS, NUL) == MISALIGNED
+    assert v(ALIGNED, 16, 4, 5, ALIGNED, *o, *WS, NUL) == INVALID              # K > E
+    assert v(ALIGNED, 16, 4, 2, ALIGNED, *o, ALIGNED, ctypes.c_size_t(8), NUL) == INVALID
     g = lib.moe_grouped_ffn_fwd_dropless
     p7 = [ALIGNED] * 7
     assert g(*p7, 16, 100, 64, 4, 2, ALIGNED, ALIGNED, NUL) == UNSUPPORTED     # H % 64

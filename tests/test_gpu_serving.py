@@ -24,7 +24,7 @@ DEV = "cuda"
 def _route(buf, logits, K, n_live=None):
     args = (buf.topk_ids, buf.topk_probs, buf.route_within, buf.route_counts, buf.sorted_slot_ids,
             buf.slot_probs, buf.expert_ids, buf.block_start, buf.token_routes,
-            buf.token_route_count, buf.num_tokens_post_padded)
+            buf.token_route_count, buf.num_tokens_post_padded, buf.workspace)
     if n_live is None:
         moe_route_dropless(logits, K, *args)
     else:

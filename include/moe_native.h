@@ -168,6 +168,26 @@ int moe_route_capacity_align(const float* logits, int64_t N, int32_t E, int32_t 
                              int32_t* token_route_count, int32_t* num_tokens_post_padded,
                              void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* moe_route_capacity_align without a workspace argument, for callers that
+ * cannot allocate device memory (code under hipGraph capture, tight serving
+ * loops, harnesses that forbid allocation): the routing map lives in a
+ * scratch array the library holds on each device it runs on, 16 MiB, until
+ * the process ends.  Same arguments (minus the workspace), same outputs bit
+ * for bit.  MOE_ERR_UNSUPPORTED when the map would not fit the array, i.e.
+ * moe_route_capacity_workspace_bytes(N, E, K) > 16 MiB (the DeepSeek-style
+ * layer, N=8192 and E=256, needs 10 MiB); MOE_ERR_LAUNCH if the array's
+ * address cannot be resolved on the current device.  Every call on one
+ * device shares that device's array: calls that overlap on one device (two
+ * streams, two host threads) race and must be ordered by the caller.  Calls
+ * no allocating routine. */
+int moe_route_capacity_align_noalloc(const float* logits, int64_t N, int32_t E, int32_t K,
+                                     int64_t C, int32_t* topk_ids, float* topk_probs,
+                                     int32_t* route_slot, int32_t* expert_count,
+                                     int32_t* sorted_slot_ids, float* slot_probs,
+                                     int32_t* expert_ids, int32_t* block_start,
+                                     int32_t* token_routes, int32_t* token_route_count,
+                                     int32_t* num_tokens_post_padded, hipStream_t stream);
+
 /* Dropless variant of steps 1-3 ([PF] sections 4-5: route_list_scan and
  * route_list_align over the routing map, with no capacity): top-K routing as
  * in moe_route_capacity, then every route is kept.

@@ -32,6 +32,7 @@ from ._native import (  # noqa: F401
     moe_route_bwd,
     moe_route_capacity,
     moe_route_capacity_align,
+    moe_route_capacity_align_noalloc,
     moe_route_capacity_workspace_bytes,
     moe_route_dropless,
     moe_route_dropless_live,

@@ -51,6 +51,8 @@ _SIGNATURES = {
     "moe_route_capacity_align": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i64, _vp, _vp, _vp, _vp,
                                                 _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                                 _vp, ctypes.c_size_t, _vp]),
+    "moe_route_capacity_align_noalloc": (ctypes.c_int, [_vp, _i64, _i32, _i32, _i64] + [_vp] * 11
+                                         + [_vp]),
     "moe_align": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i64,
                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_grouped_ffn_fwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64,
@@ -197,6 +199,30 @@ def moe_route_capacity_align(logits, K: int, C: int, topk_ids, topk_probs, route
         _ptr(token_route_count, torch.int32, N, "token_route_count"),
         _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"),
         *_ws(workspace, N, E, K), _stream(stream)))
+
+
+def moe_route_capacity_align_noalloc(logits, K: int, C: int, topk_ids, topk_probs, route_slot,
+                                     expert_count, sorted_slot_ids, slot_probs, expert_ids,
+                                     block_start, token_routes, token_route_count,
+                                     num_tokens_post_padded, stream=None):
+    """moe_route_capacity_align with the routing map in the library's own
+    per-device scratch array (no workspace, nothing allocated)."""
+    N, E = logits.shape
+    R = E * moe_padded_capacity(C)
+    BM = moe_layout_block_m()
+    _check("moe_route_capacity_align_noalloc", lib.moe_route_capacity_align_noalloc(
+        _ptr(logits, torch.float32, N * E, "logits"), N, E, K, C,
+        _ptr(topk_ids, torch.int32, N * K, "topk_ids"),
+        _ptr(topk_probs, torch.float32, N * K, "topk_probs"),
+        _ptr(route_slot, torch.int32, N * K, "route_slot"),
+        _ptr(expert_count, torch.int32, E, "expert_count"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"),
+        _ptr(slot_probs, torch.float32, R, "slot_probs"),
+        _ptr(expert_ids, torch.int32, R // BM, "expert_ids"),
+        _ptr(block_start, torch.int32, E, "block_start"),
+        _ptr(token_routes, torch.int32, N * K, "token_routes"),
+        _ptr(token_route_count, torch.int32, N, "token_route_count"),
+        _ptr(num_tokens_post_padded, torch.int32, 1, "num_tokens_post_padded"), _stream(stream)))
 
 
 def moe_align(topk_ids, topk_probs, route_slot, expert_count, N: int, E: int, K: int, C: int,

@@ -739,3 +739,60 @@ extern "C" int moe_route_dropless_live(const float* logits, int64_t N, int32_t E
                                token_routes, token_route_count, num_tokens_post_padded, workspace,
                                workspace_bytes, stream);
 }
+
+// ---------------------------------------------------------------------------
+// Allocation-free routing: moe_route_capacity_align with the routing map in a
+// library-owned scratch array instead of a caller workspace, for callers that
+// cannot allocate.  Each device holds its own copy of the array (until the
+// process ends); host code reaches it only through the address
+// hipGetSymbolAddress returns on that device, resolved on the first call made
+// there and kept per device.  Every call on a device reuses the same array:
+// each call overwrites the map rows it reads (nothing must start at zero),
+// and calls that overlap on one device race.
+// ---------------------------------------------------------------------------
+namespace moe {
+namespace {
+
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// The scratch array's device address on the current device, or null.
+void* scratch_on_current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (p) return p;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+    return p;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_route_capacity_align_noalloc(const float* logits, int64_t N, int32_t E, int32_t K,
+                                                int64_t C, int32_t* topk_ids, float* topk_probs,
+                                                int32_t* route_slot, int32_t* expert_count,
+                                                int32_t* sorted_slot_ids, float* slot_probs,
+                                                int32_t* expert_ids, int32_t* block_start,
+                                                int32_t* token_routes, int32_t* token_route_count,
+                                                int32_t* num_tokens_post_padded, hipStream_t stream) {
+    using namespace moe;
+    int st = check_route_shape(N, E, K, C);
+    if (st != MOE_OK) return st;
+    if (N == 0) return MOE_OK;
+    st = check_route_ptrs({logits, topk_ids, topk_probs, route_slot, expert_count, sorted_slot_ids,
+                           slot_probs, expert_ids, block_start, token_routes, token_route_count,
+                           num_tokens_post_padded});
+    if (st != MOE_OK) return st;
+    if (map_bytes(N, E) > kScratchBytes) return MOE_ERR_UNSUPPORTED;
+    void* ws = scratch_on_current_device();
+    if (!ws) return MOE_ERR_LAUNCH;
+    return moe_route_capacity_align(logits, N, E, K, C, topk_ids, topk_probs, route_slot, expert_count,
+                                    sorted_slot_ids, slot_probs, expert_ids, block_start, token_routes,
+                                    token_route_count, num_tokens_post_padded, ws, kScratchBytes,
+                                    stream);
+}

@@ -27,7 +27,8 @@ def test_every_declared_symbol_is_exported():
                           "moe_grouped_fc2_dgrad", "moe_swiglu_bwd", "moe_grouped_fc1_dgrad",
                           "moe_grouped_fc2_wgrad", "moe_grouped_fc1_wgrad", "moe_route_bwd",
                           "moe_route_dropless_live", "moe_dispatch_rows",
-                          "moe_grouped_fc2_rows", "moe_route_capacity_workspace_bytes"}
+                          "moe_grouped_fc2_rows", "moe_route_capacity_workspace_bytes",
+                          "moe_route_capacity_align_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -118,6 +119,16 @@ def test_route_capacity_align_validation():
     assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o[:2], NUL, *o[3:], *WS, NUL) == INVALID
     assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o, ALIGNED, ctypes.c_size_t(319), NUL) == INVALID
     assert f(NUL, 0, 4, 2, 0, *([NUL] * 4), *([NUL] * 7), NUL, ctypes.c_size_t(0), NUL) == OK   # N = 0
+
+
+def test_route_noalloc_validation():
+    f = lib.moe_route_capacity_align_noalloc
+    o = [ALIGNED] * 7
+    assert f(ALIGNED, 16, 4, 5, 20, *([ALIGNED] * 4), *o, NUL) == INVALID                 # K > E
+    assert f(ALIGNED, 16, 4, 2, 8, *([ALIGNED] * 4), *o[:6], MIS, NUL) == MISALIGNED
+    # the map must fit the 16 MiB scratch array: 5 * 1024 * 16384 bytes does not
+    assert f(ALIGNED, 16384, 1024, 8, 128, *([ALIGNED] * 4), *o, NUL) == UNSUPPORTED
+    assert f(NUL, 0, 4, 2, 0, *([NUL] * 4), *([NUL] * 7), NUL) == OK                       # N = 0
 
 
 def test_dropless_bound_and_validation():

@@ -157,6 +157,21 @@ def vendor_reference(torch, moe, w, args):
         out[name] = {"shape": [w.E, M, N, K], "us": us, "tflops": 2.0 * w.E * M * N * K / us / 1e6}
         log(f"[bench] vendor bmm {name} {w.E}x({M}x{N}x{K}): {us:.1f} us, {out[name]['tflops']:.0f} TFLOP/s")
         del a, b
+    # a large square product: what a bf16 GEMM with no gather reaches on this device
+    g = torch.Generator(device="cuda").manual_seed(8)
+    a = torch.randn(8192, 8192, generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn(8192, 8192, generator=g, device="cuda").to(torch.bfloat16)
+    with torch.cuda.stream(stream):
+        warm(lambda: torch.mm(a, b), args.warmup, args.warmup_seconds, stream)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(stream)
+        for _ in range(args.steps):
+            torch.mm(a, b)
+        ev1.record(stream)
+        stream.synchronize()
+    us = ev0.elapsed_time(ev1) / args.steps * 1e3
+    out["square_8192"] = {"shape": [1, 8192, 8192, 8192], "us": us, "tflops": 2.0 * 8192 ** 3 / us / 1e6}
+    log(f"[bench] vendor mm 8192^3: {us:.1f} us, {out['square_8192']['tflops']:.0f} TFLOP/s")
     print(json.dumps(out))
 
 
@@ -178,6 +193,36 @@ def copy_rate(torch, stream, nbytes=1 << 30, reps=10):
     del src, dst
     log(f"[bench] device copy: {gbs:.0f} GB/s")
     return gbs
+
+
+def hbm_probes(torch, moe, stream, nbytes=2 << 30, reps=10):
+    """GB/s this device's HBM reaches for a plain streaming read, streaming
+    write and copy (the library's probe kernels, 2 GiB buffers; bytes moved:
+    read and write count once, the copy twice).  These are the measured
+    ceilings the layer's kernels are set against; the published 8 TB/s is
+    nominal."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    calls = {"read": (lambda: moe.moe_probe_read(src, sink, stream), nbytes),
+             "write": (lambda: moe.moe_probe_write(dst, stream), nbytes),
+             "copy": (lambda: moe.moe_probe_copy(src, dst, stream), 2 * nbytes)}
+    out = {}
+    with torch.cuda.stream(stream):
+        moe.moe_probe_write(src, stream)
+        for name, (fn, moved) in calls.items():
+            for _ in range(3):
+                fn()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(reps):
+                fn()
+            ev1.record(stream)
+            stream.synchronize()
+            out[name] = moved * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst, sink
+    log("[bench] HBM probes GB/s: " + ", ".join(f"{k} {v:.0f}" for k, v in out.items()))
+    return out
 
 
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
@@ -253,17 +298,39 @@ def time_graph(torch, step, stream, args, stats=None):
     ms = ev0.elapsed_time(ev1) / args.steps
     log(f"[bench] graph replay: {ms * 1e3:.1f} us/step (wall {wall / args.steps * 1e6:.1f} us)")
     if stats is not None:
+        # Single replays, each between its own pair of events.  The timed
+        # replays are queued behind untimed ones, so the host is ahead of the
+        # GPU throughout and each interval holds one replay's kernels and the
+        # graph's launch gap on the device, not the host's enqueue latency.
         with torch.cuda.stream(stream):
             evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            for _ in range(8):
+                graph.replay()
             evs[0].record(stream)
             for i in range(args.steps):
                 graph.replay()
                 evs[i + 1].record(stream)
             stream.synchronize()
-        each = sorted(evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps))
-        stats["median"] = statistics.median(each)
-        stats["p90"] = each[min(len(each) - 1, int(0.9 * len(each)))]
-        log(f"[bench] single replays: median {stats['median']:.1f} us, p90 {stats['p90']:.1f} us")
+        each = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)]
+        srt = sorted(each)
+        q = lambda f: srt[min(len(srt) - 1, int(f * len(srt)))]     # noqa: E731
+        stats.update({"interval": "device time of one replay, replays queued back to back",
+                      "median": statistics.median(srt), "p90": q(0.9), "p99": q(0.99), "max": srt[-1],
+                      "all": [round(v, 1) for v in each]})
+        # host-inclusive latency: launch one replay and wait for it
+        host = []
+        with torch.cuda.stream(stream):
+            for _ in range(min(args.steps, 50)):
+                t0 = time.perf_counter()
+                graph.replay()
+                stream.synchronize()
+                host.append((time.perf_counter() - t0) * 1e6)
+        host.sort()
+        stats["host_launch_to_done_us"] = {"median": statistics.median(host),
+                                           "p90": host[min(len(host) - 1, int(0.9 * len(host)))]}
+        log(f"[bench] single replays: median {stats['median']:.1f} us, p90 {stats['p90']:.1f}, "
+            f"p99 {stats['p99']:.1f}, max {stats['max']:.1f}; launch-to-done on the host "
+            f"{stats['host_launch_to_done_us']['median']:.1f} us")
     return ms
 
 
@@ -294,7 +361,7 @@ def time_calls(torch, names, calls, stream, args):
     return us
 
 
-def roofline(name, flops, nbytes, us, traffic=None):
+def roofline(name, flops, nbytes, us, traffic=None, probes=None):
     """Roofline of one kernel: its bound is whichever resource needs the
     longer time at peak; `achieved` is the algorithmic work per launch over
     the launch time, against that resource's peak."""
@@ -305,6 +372,10 @@ def roofline(name, flops, nbytes, us, traffic=None):
     common = {"kernel": name, "traffic": traffic, "algorithmic_bytes": nbytes, "flops": flops,
               "launch_us": us, "arithmetic_intensity": flops / nbytes,
               "attainable_frac": max(t_hbm, t_mfma) / (us * 1e-6)}
+    if probes:
+        # against what this device's HBM sustains (the probes), not the nominal peak
+        common["measured_ceiling_gbs"] = {"read": probes["read"], "copy": probes["copy"]}
+        common["frac_of_measured_read"] = gbs / probes["read"]
     if t_hbm >= t_mfma:
         return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": gbs / PEAK_HBM_GBS, "mfma_tflops": tflops,
@@ -721,6 +792,7 @@ def main():
     replay = {}
     ms_per_step = time_graph(torch, fwd, stream, args, replay)
     us = time_calls(torch, names, calls, stream, args)
+    probes = hbm_probes(torch, moe, stream)
 
     kept = int((buf.token_routes >= 0).sum().item())
     if dropless:
@@ -766,12 +838,20 @@ def main():
         # the scan / scatter / gather steps together (routing call + combine)
         "route_combine_frac_hbm_peak": (nbytes[route_name] + nbytes["combine"])
                                        / ((us[route_name] + us["combine"]) * 1e-6) / 1e9 / PEAK_HBM_GBS,
-        # torch's own device copy: a reference point for HBM rates, not a
-        # ceiling (the combine kernel runs above it)
+        # torch's own device copy: a reference point for HBM rates
         "torch_copy_gbs": copy_rate(torch, stream),
+        # the measured ceilings (the library's HBM probes), and each call's
+        # rate of algorithmic bytes against the probe read and copy rates
+        "hbm_probe_gbs": probes,
+        "kernel_frac_probe": {n: {"read": gbs[n] / probes["read"], "copy": gbs[n] / probes["copy"]}
+                              for n in names},
+        # the combine reads route_out right after FC2 wrote it; most of those
+        # 134 MB come from the 256 MB last-level cache, so its rate is an
+        # effective, cache-assisted one, not an HBM-efficiency figure
+        "combine_rate_note": "effective (cache-assisted): route_out is read from the last-level cache FC2 just filled",
         "kept_routes": kept,
         "roofline": roofline("fc1_swiglu (gather-in-GEMM FC1 + SwiGLU*prob)", fc1_flops,
-                             nbytes["fc1"], us["fc1"], traffic),
+                             nbytes["fc1"], us["fc1"], traffic, probes),
     }
     if not args.no_cpu_baseline:
         log("[bench] cpu_baseline: timing the oracle")

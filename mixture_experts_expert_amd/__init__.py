@@ -29,6 +29,10 @@ from ._native import (  # noqa: F401
     moe_grouped_ffn_fwd_dropless,
     moe_layout_block_m,
     moe_padded_capacity,
+    moe_probe_copy,
+    moe_probe_read,
+    moe_probe_write,
+    PROBE_HEADER_PATH,
     moe_route_bwd,
     moe_route_capacity,
     moe_route_capacity_align,

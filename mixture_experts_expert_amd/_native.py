@@ -19,6 +19,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libmoe_native.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_native.h")
+PROBE_HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "moe_probe.h")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -74,6 +75,9 @@ _SIGNATURES = {
     "moe_grouped_fc1_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp,
                                              _vp]),
     "moe_route_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i64, _vp, _vp]),
+    "moe_probe_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _vp]),
+    "moe_probe_write": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp]),
+    "moe_probe_copy": (ctypes.c_int, [_vp, _vp, ctypes.c_size_t, _vp]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -82,10 +86,37 @@ for _name, (_res, _args) in _SIGNATURES.items():
 
 
 def header_functions(path: str = HEADER_PATH):
-    """Names of the functions include/moe_native.h declares."""
+    """Names of the functions a header (default include/moe_native.h) declares."""
     text = open(path).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def _bytes_ptr(t: torch.Tensor, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+    return ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size()
+
+
+def moe_probe_read(src, sink, stream=None):
+    """Stream-read all of src once (an HBM rate probe); sink: int32 device tensor."""
+    p, n = _bytes_ptr(src, "src")
+    _check("moe_probe_read", lib.moe_probe_read(p, n, _bytes_ptr(sink, "sink")[0], _stream(stream)))
+
+
+def moe_probe_write(dst, stream=None):
+    """Stream-write all of dst once (an HBM rate probe)."""
+    p, n = _bytes_ptr(dst, "dst")
+    _check("moe_probe_write", lib.moe_probe_write(p, n, _stream(stream)))
+
+
+def moe_probe_copy(src, dst, stream=None):
+    """dst = src, byte for byte (an HBM rate probe); equal sizes."""
+    ps, n = _bytes_ptr(src, "src")
+    pd, m = _bytes_ptr(dst, "dst")
+    if n != m:
+        raise ValueError("moe_probe_copy: src and dst differ in size")
+    _check("moe_probe_copy", lib.moe_probe_copy(ps, pd, n, _stream(stream)))
 
 
 class MoEError(RuntimeError):

@@ -33,6 +33,21 @@ def test_every_declared_symbol_is_exported():
         assert hasattr(lib, n), n
 
 
+def test_probe_header_symbols_and_validation():
+    names = moe.header_functions(moe.PROBE_HEADER_PATH)
+    assert set(names) == {"moe_probe_read", "moe_probe_write", "moe_probe_copy"}
+    for n in names:
+        assert hasattr(lib, n), n
+    big = ctypes.c_size_t(1 << 20)
+    assert lib.moe_probe_read(NUL, big, ALIGNED, NUL) == INVALID
+    assert lib.moe_probe_read(ALIGNED, big, NUL, NUL) == INVALID
+    assert lib.moe_probe_read(MIS, big, ALIGNED, NUL) == MISALIGNED
+    assert lib.moe_probe_write(ALIGNED, ctypes.c_size_t(17), NUL) == MISALIGNED
+    assert lib.moe_probe_copy(ALIGNED, MIS, big, NUL) == MISALIGNED
+    assert lib.moe_probe_copy(ALIGNED, ALIGNED, ctypes.c_size_t(0), NUL) == OK
+    assert lib.moe_probe_write(ALIGNED, ctypes.c_size_t(0), NUL) == OK
+
+
 def test_capacity_golden_values():
     for c in load_golden("capacity_closed_form.json")["cases"]:
         assert moe.moe_source_capacity(c["N"], c["K"], c["E"], c["F"]) == c["C"], c

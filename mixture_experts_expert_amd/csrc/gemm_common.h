@@ -21,6 +21,8 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (CDNA
 // An offset past every descriptor used here (each covers < 2 GiB): a load
 // from it returns zeros without touching memory, a store to it is dropped.
 constexpr uint32_t kOob = 0x80000000u;
+// cache-policy operand of a buffer store: non-temporal (streamed)
+constexpr int kStoreNT = 2;
 
 __device__ __forceinline__ int xcd_remap(int bid, int G) {
     const int q = G / kXcds, r = G % kXcds;

@@ -72,9 +72,6 @@ struct BwdArgs {
 
 typedef const __attribute__((address_space(4))) int* const_int_ptr;
 
-// cache-policy operand of a buffer store: non-temporal (streamed)
-constexpr int kStoreNT = 2;
-
 // Data gradient: out rows are the expert's slots, A is row-major by slot
 // (the expert's segment of a route-ordered buffer, or gathered token rows),
 // B is the expert's weight matrix, K-major.

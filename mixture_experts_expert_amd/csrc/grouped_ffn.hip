@@ -29,9 +29,12 @@
 //     only the I-wide bf16 activation is written;
 //   * tiles are renumbered so that consecutive tiles (same expert, adjacent
 //     N-tiles, sharing the gathered A rows) land on the same XCD and its L2;
-//   * FC2 over whole 256-row tiles runs on the producer/consumer slot GEMM
-//     (slot_gemm.h): waves that only load and waves that only compute and
-//     store, so the route_out stores never hold up a load wait.
+//   * 256x256 tiles leave through a staged epilogue: the tile is written
+//     into the two LDS stages its last K step freed and goes out in whole
+//     128-byte lines, which disturbs the load stream far less than 32-byte
+//     pieces straight from the accumulator layout;
+//   * FC2 with an output row map (an expert-parallel rank's return layout)
+//     runs on the producer/consumer slot GEMM (slot_gemm.h).
 #include <algorithm>
 #include <atomic>
 #include <cmath>
@@ -80,7 +83,7 @@ struct FfnArgs {
 // a swap of lane halves leaves 8 consecutive bf16 columns per lane for one
 // 16-byte store.
 template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1, bool DYN,
-          bool SAVE = false>
+          bool SAVE = false, int EPI = 0>
 __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     constexpr int NW = WM * WN;
     constexpr int WTM = BMT / WM;
@@ -115,6 +118,12 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
                   "whole DMA blocks per wave");
     static_assert(NA >= 2 && NB >= 2 && WAIT + STORES < 64, "stage rings");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
+    // Staged epilogue (EPI 1: default store policy, 2: non-temporal): the
+    // tile leaves through the A and B stages its last K step freed.  FC1
+    // stages the whole 256 x 128 activation tile (A stage rows 0-127, B stage
+    // rows 128-255); FC2 gives each wave 8 KB of them for its 128 x 64 piece.
+    static_assert(EPI == 0 || (BMT == 256 && BNT == 256 && BK == 64 && WM == 2 && WN == 4 && !SAVE),
+                  "staged epilogue shape");
     static_assert(!DYN || LDS_BYTES >= (3 * kMaxE + 1) * 4, "room for the tile list");
 
     __shared__ __attribute__((aligned(1024))) uint8_t smem[LDS_BYTES];
@@ -488,73 +497,143 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
         const __amdgpu_buffer_rsrc_t prsrc = __builtin_amdgcn_make_buffer_rsrc(
             SAVE ? p.preact + static_cast<int64_t>(cur.seg) * 2 * p.ncols : p.out, static_cast<short>(0),
             SAVE ? cur.len * p.ncols * 4 : 0, kRsrcWord3);
+        // FC1: the lane's 8 activations of block (mi, ni), tile columns
+        // (wn*WTN + ni*32)/2 + 8*half ..
+        auto fc1_act = [&](int mi, int ni) {
+            const floatx16& v = acc[mi][ni];
+            uint32_t x[2], y[2];
 #pragma unroll
-        for (int mi = 0; mi < MI; ++mi) {
-            const int row = cur.m0 + wm * WTM + mi * 32 + (lane & 31);   // slot within the expert
+            for (int q = 0; q < 2; ++q) {
+                x[q] = pack_bf16x2(silu(v[2 * q]) * v[2 * q + 8] * prob[mi],
+                                   silu(v[2 * q + 1]) * v[2 * q + 9] * prob[mi]);
+                y[q] = pack_bf16x2(silu(v[2 * q + 4]) * v[2 * q + 12] * prob[mi],
+                                   silu(v[2 * q + 5]) * v[2 * q + 13] * prob[mi]);
+            }
+            const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+            u32x4 d;
+            d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
+            return d;
+        };
+        // FC2: the lane's 8 outputs of block (mi, ni), half q: the wave's
+        // columns ni*32 + 16q + 8*half ..
+        auto fc2_out = [&](int mi, int ni, int q) {
+            uint32_t g[2][2];
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni) {
-                if (FC1) {
-                    uint32_t x[2], y[2];
+            for (int h = 0; h < 2; ++h) {
+                g[h][0] = pack_bf16x2(acc[mi][ni][8 * q + 4 * h], acc[mi][ni][8 * q + 4 * h + 1]);
+                g[h][1] = pack_bf16x2(acc[mi][ni][8 * q + 4 * h + 2], acc[mi][ni][8 * q + 4 * h + 3]);
+            }
+            const auto s0 = __builtin_amdgcn_permlane32_swap(g[0][0], g[1][0], false, false);
+            const auto s1 = __builtin_amdgcn_permlane32_swap(g[0][1], g[1][1], false, false);
+            u32x4 d;
+            d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
+            return d;
+        };
+        if constexpr (EPI != 0) {
+            constexpr int POLICY = EPI == 2 ? kStoreNT : 0;
+            typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+            __syncthreads();                                // every wave is past the last K step
+            const uint32_t rA = static_cast<uint32_t>(a_fill), rB = static_cast<uint32_t>(B_RING + b_fill);
+            if constexpr (FC1) {
+                // tile row tr (256 bytes: 16 chunks, swizzled by row) of the
+                // staged activation tile; 16 lanes then write each row whole
+                auto so = [&](int tr, int c) {
+                    const int rr = tr & 127;
+                    return (tr < 128 ? rA : rB) + static_cast<uint32_t>(rr * 256 + ((c ^ (rr & 15)) << 4));
+                };
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const floatx16& v = acc[mi][ni];
-                        const float a0 = silu(v[2 * q]) * v[2 * q + 8] * prob[mi];
-                        const float a1 = silu(v[2 * q + 1]) * v[2 * q + 9] * prob[mi];
-                        const float b0 = silu(v[2 * q + 4]) * v[2 * q + 12] * prob[mi];
-                        const float b1 = silu(v[2 * q + 5]) * v[2 * q + 13] * prob[mi];
-                        x[q] = pack_bf16x2(a0, a1);
-                        y[q] = pack_bf16x2(b0, b1);
-                    }
-                    u32x4 d;
-                    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
-                    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
-                    d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
-                    const int col = cur.nt * OUT_COLS + (wn * WTN + ni * 32) / 2 + 8 * half;
-                    const bool live = row < cur.len && col < p.ncols;
-                    const uint32_t off = live ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
-                    __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
-                    if (SAVE) {
-                        // the same columns of the raw gate (acc[0..7]) and up
-                        // (acc[8..15]) rows, at col and I + col of the row
-                        const floatx16& v = acc[mi][ni];
-                        uint32_t gx[2], gy[2], ux[2], uy[2];
+                for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            gx[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
-                            gy[q] = pack_bf16x2(v[2 * q + 4], v[2 * q + 5]);
-                            ux[q] = pack_bf16x2(v[2 * q + 8], v[2 * q + 9]);
-                            uy[q] = pack_bf16x2(v[2 * q + 12], v[2 * q + 13]);
-                        }
-                        const auto g0 = __builtin_amdgcn_permlane32_swap(gx[0], gy[0], false, false);
-                        const auto g1 = __builtin_amdgcn_permlane32_swap(gx[1], gy[1], false, false);
-                        const auto u0 = __builtin_amdgcn_permlane32_swap(ux[0], uy[0], false, false);
-                        const auto u1 = __builtin_amdgcn_permlane32_swap(ux[1], uy[1], false, false);
-                        u32x4 dg, du;
-                        dg[0] = g0[0]; dg[1] = g1[0]; dg[2] = g0[1]; dg[3] = g1[1];
-                        du[0] = u0[0]; du[1] = u1[0]; du[2] = u0[1]; du[3] = u1[1];
-                        const uint32_t poff = live
-                            ? (static_cast<uint32_t>(row) * 2u * p.ncols + col) * 2u : kOob;
-                        __builtin_amdgcn_raw_buffer_store_b128(dg, prsrc, poff, 0, 0);
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            du, prsrc, live ? poff + static_cast<uint32_t>(p.ncols) * 2u : kOob, 0, 0);
-                    }
-                } else {
-                    uint32_t g[4][2];
+                    for (int ni = 0; ni < NI; ++ni)
+                        *(lds_u32x4*)((lds_u8*)smem + so(wm * WTM + mi * 32 + (lane & 31),
+                                                         ((wn * WTN + ni * 32) / 2 + 8 * half) / 8)) = fc1_act(mi, ni);
+                __syncthreads();
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        g[q][0] = pack_bf16x2(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1]);
-                        g[q][1] = pack_bf16x2(acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
-                    }
+                for (int j = 0; j < BMT / NW / 4; ++j) {
+                    const int tr = wave * (BMT / NW) + j * 4 + lane / 16, c = lane % 16;
+                    const u32x4 v = *(const lds_u32x4*)((lds_u8*)smem + so(tr, c));
+                    const int row = cur.m0 + tr, col = cur.nt * OUT_COLS + c * 8;
+                    const uint32_t off = row < cur.len && col < p.ncols
+                        ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, off, 0, POLICY);
+                }
+            } else {
+                // the wave's 8 KB, 64 rows of 128 bytes (its 64 columns, 8
+                // chunks swizzled by row) per round, two row blocks a round;
+                // the wave reads back what its other lanes wrote (LDS
+                // operations of one wave complete in order; the clobbers keep
+                // the compiler from moving them across)
+                const uint32_t base = wave < NW / 2 ? rA + wave * 8192u : rB + (wave - NW / 2) * 8192u;
+                auto so = [&](int r, int c) { return base + static_cast<uint32_t>(r * 128 + ((c ^ (r & 7)) << 4)); };
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const auto s0 = __builtin_amdgcn_permlane32_swap(g[2 * q][0], g[2 * q + 1][0], false, false);
-                        const auto s1 = __builtin_amdgcn_permlane32_swap(g[2 * q][1], g[2 * q + 1][1], false, false);
-                        u32x4 d;
-                        d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
-                        const int col = cur.nt * OUT_COLS + wn * WTN + ni * 32 + 16 * q + 8 * half;
+                for (int h = 0; h < MI / 2; ++h) {
+                    asm volatile("" ::: "memory");
+#pragma unroll
+                    for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+                        for (int ni = 0; ni < NI; ++ni)
+#pragma unroll
+                            for (int q = 0; q < 2; ++q)
+                                *(lds_u32x4*)((lds_u8*)smem + so(m2 * 32 + (lane & 31), ni * 4 + 2 * q + half)) =
+                                    fc2_out(2 * h + m2, ni, q);
+                    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                    for (int j = 0; j < 8; ++j) {
+                        const int r = j * 8 + lane / 8, c = lane % 8;
+                        const u32x4 v = *(const lds_u32x4*)((lds_u8*)smem + so(r, c));
+                        const int row = cur.m0 + wm * WTM + h * 64 + r, col = cur.nt * OUT_COLS + wn * WTN + c * 8;
                         const uint32_t off = row < cur.len && col < p.ncols
                             ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
-                        __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, off, 0, POLICY);
+                    }
+                    asm volatile("" ::: "memory");
+                }
+            }
+        } else {
+#pragma unroll
+            for (int mi = 0; mi < MI; ++mi) {
+                const int row = cur.m0 + wm * WTM + mi * 32 + (lane & 31);   // slot within the expert
+#pragma unroll
+                for (int ni = 0; ni < NI; ++ni) {
+                    if (FC1) {
+                        const int col = cur.nt * OUT_COLS + (wn * WTN + ni * 32) / 2 + 8 * half;
+                        const bool live = row < cur.len && col < p.ncols;
+                        const uint32_t off = live ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
+                        __builtin_amdgcn_raw_buffer_store_b128(fc1_act(mi, ni), orsrc, off, 0, 0);
+                        if (SAVE) {
+                            // the same columns of the raw gate (acc[0..7]) and up
+                            // (acc[8..15]) rows, at col and I + col of the row
+                            const floatx16& v = acc[mi][ni];
+                            uint32_t gx[2], gy[2], ux[2], uy[2];
+#pragma unroll
+                            for (int q = 0; q < 2; ++q) {
+                                gx[q] = pack_bf16x2(v[2 * q], v[2 * q + 1]);
+                                gy[q] = pack_bf16x2(v[2 * q + 4], v[2 * q + 5]);
+                                ux[q] = pack_bf16x2(v[2 * q + 8], v[2 * q + 9]);
+                                uy[q] = pack_bf16x2(v[2 * q + 12], v[2 * q + 13]);
+                            }
+                            const auto g0 = __builtin_amdgcn_permlane32_swap(gx[0], gy[0], false, false);
+                            const auto g1 = __builtin_amdgcn_permlane32_swap(gx[1], gy[1], false, false);
+                            const auto u0 = __builtin_amdgcn_permlane32_swap(ux[0], uy[0], false, false);
+                            const auto u1 = __builtin_amdgcn_permlane32_swap(ux[1], uy[1], false, false);
+                            u32x4 dg, du;
+                            dg[0] = g0[0]; dg[1] = g1[0]; dg[2] = g0[1]; dg[3] = g1[1];
+                            du[0] = u0[0]; du[1] = u1[0]; du[2] = u0[1]; du[3] = u1[1];
+                            const uint32_t poff = live
+                                ? (static_cast<uint32_t>(row) * 2u * p.ncols + col) * 2u : kOob;
+                            __builtin_amdgcn_raw_buffer_store_b128(dg, prsrc, poff, 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                du, prsrc, live ? poff + static_cast<uint32_t>(p.ncols) * 2u : kOob, 0, 0);
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int col = cur.nt * OUT_COLS + wn * WTN + ni * 32 + 16 * q + 8 * half;
+                            const uint32_t off = row < cur.len && col < p.ncols
+                                ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
+                            __builtin_amdgcn_raw_buffer_store_b128(fc2_out(mi, ni, q), orsrc, off, 0, 0);
+                        }
                     }
                 }
             }
@@ -581,10 +660,10 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
 }
 
 template <int BMT, int BNT, int WM, int WN, int BK, int NA, int NB, bool FC1, bool DYN,
-          bool SAVE = false>
+          bool SAVE = false, int EPI = 0>
 void launch_persistent(const FfnArgs& a, hipStream_t s) {
     constexpr int threads = WM * WN * kWave;
-    auto* k = ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, FC1, DYN, SAVE>;
+    auto* k = ffn_gemm_kernel<BMT, BNT, WM, WN, BK, NA, NB, FC1, DYN, SAVE, EPI>;
     static std::atomic<int> occupancy{0};   // workgroups per CU (LDS and registers decide it)
     int occ = occupancy.load(std::memory_order_relaxed);
     if (occ == 0) {
@@ -611,9 +690,14 @@ int launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s, bool dyn = false) {
         if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, true>(a, s);
         else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, true>(a, s);
     } else {
+        // 256 x 256 tiles leave through the staged epilogue: FC1's
+        // activation non-temporal (FC2 reads it from HBM at no measured
+        // cost), FC2's route_out with the default policy (the combine reads
+        // it next, partly from cache)
+        constexpr bool STAGED = BMT == 256 && BNT == 256 && BK == 64 && WM == 2 && WN == 4;
         if (fc1 && a.preact) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false, true>(a, s);
-        else if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false>(a, s);
-        else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, false>(a, s);
+        else if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false, false, STAGED ? 2 : 0>(a, s);
+        else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, false, false, STAGED ? 1 : 0>(a, s);
     }
     return MOE_OK;
 }
@@ -649,12 +733,8 @@ int pick_tile_dyn(double mean) {
     return 32;
 }
 
-// Fixed segments tile Cp; variable ones (dyn) take their shape from the mean
-// number of routes per expert, which only steers performance.
-// FC2 over whole 256-row tiles runs on the producer/consumer slot GEMM: its
-// loading waves never wait on the route_out stores (same tiles, same K
-// order, the same results bit for bit as the one-role kernel, a few percent
-// faster).
+// FC2 with an output row map runs on the producer/consumer slot GEMM (same
+// tiles, same K order: the same products bit for bit as the one-role kernel).
 int launch_fc2_slots(const FfnArgs& a, int E, hipStream_t s, const int* out_rows = nullptr) {
     SlotArgs sa{};
     sa.a = a.a; sa.b = a.w; sa.out = a.out;
@@ -676,8 +756,10 @@ int launch_fc2_slots(const FfnArgs& a, int E, hipStream_t s, const int* out_rows
     return MOE_OK;
 }
 
+// Fixed segments tile Cp; variable ones (dyn) take their shape from the mean
+// number of routes per expert, which only steers performance.
 int launch(const FfnArgs& a, bool fc1, int E, hipStream_t s, bool dyn = false, double mean = 0.0) {
-    if (!fc1 && !dyn && a.Kdim >= 128 && pick_tile_m(a.Cp) == 256) return launch_fc2_slots(a, E, s);
+
     if (a.Kdim < 128) {
         // a 64-long contraction: 32-wide K slabs, so a tile has the two
         // steps the cross-tile look-ahead needs

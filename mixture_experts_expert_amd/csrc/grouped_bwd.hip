@@ -224,14 +224,25 @@ __global__ __launch_bounds__(WM * WN * kWave) void dgrad_kernel(BwdArgs p) {
     }
 
     // ---- epilogue: lane (row l&31, half h) holds columns 8g + 4h + (0..3)
-    // of each 32-column block in acc[4g .. 4g+3]; bf16, half swap, 16-byte
-    // stores.  Rows and columns past the output get an offset beyond the
-    // descriptor: the store is dropped.
+    // of each 32-column block in acc[4g .. 4g+3]; bf16 and a swap of lane
+    // halves give each lane 8 consecutive columns.  The workgroup's last
+    // loads (past K: zeros into stages nobody reads) land first; then each
+    // wave stages its WTM x WTN piece in its own part of the idle rings
+    // (16-byte chunks swizzled by row) and writes it out in whole rows of
+    // WTN*2 bytes (straight from the accumulators, one store would write
+    // 32-byte pieces of 32 rows).  Rows and columns past the output get an
+    // offset beyond the descriptor: the store is dropped.
+    static_assert(NW * WTM * WTN * 2 <= LDS_BYTES, "staging fits the rings");
+    constexpr int CPRO = WTN / 8;                  // 16-byte chunks per staged row
+    wait_vmcnt<0>();
+    __syncthreads();
     const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
         p.out + static_cast<int64_t>(seg) * p.ldo, static_cast<short>(0), len * p.ldo * 2, kRsrcWord3);
+    typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+    lds_u8* st = (lds_u8*)smem + wave * (WTM * WTN * 2);
+    auto so = [](int r, int c) { return static_cast<uint32_t>(r * (WTN * 2) + ((c ^ (r % CPRO)) << 4)); };
 #pragma unroll
     for (int mi = 0; mi < MI; ++mi) {
-        const int row = m0 + wm * WTM + mi * 32 + (lane & 31);
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
             uint32_t g[4][2];
@@ -246,14 +257,23 @@ __global__ __launch_bounds__(WM * WN * kWave) void dgrad_kernel(BwdArgs p) {
                 const auto s1 = __builtin_amdgcn_permlane32_swap(g[2 * q][1], g[2 * q + 1][1], false, false);
                 u32x4 d;
                 d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
-                const int col = n0 + wn * WTN + ni * 32 + 16 * q + 8 * half;
-                const uint32_t off = row < len && col < p.Nn
-                    ? (static_cast<uint32_t>(row) * p.ldo + col) * 2u : kOob;
-                __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
+                // columns ni*32 + 16q + 8*half of the wave's WTN
+                *(lds_u32x4*)(st + so(mi * 32 + (lane & 31), ni * 4 + 2 * q + half)) = d;
             }
         }
     }
-    wait_vmcnt<0>();   // no DMA may still be writing LDS when the workgroup ends
+    // the wave reads back what its other lanes wrote: LDS operations of one
+    // wave complete in order, and the clobbers keep the compiler from moving
+    // them across
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < WTM * CPRO / kWave; ++j) {
+        const int r = j * (kWave / CPRO) + lane / CPRO, c = lane % CPRO;
+        const u32x4 v = *(const lds_u32x4*)(st + so(r, c));
+        const int row = m0 + wm * WTM + r, col = n0 + wn * WTN + c * 8;
+        const uint32_t off = row < len && col < p.Nn ? (static_cast<uint32_t>(row) * p.ldo + col) * 2u : kOob;
+        __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, off, 0, 0);
+    }
 }
 
 // ---- weight gradient.  dW[e][m, n] = sum over the expert's slots s of

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     // tile leaves through the A and B stages its last K step freed.  FC1
     // stages the whole 256 x 128 activation tile (A stage rows 0-127, B stage
     // rows 128-255); FC2 gives each wave 8 KB of them for its 128 x 64 piece.
-    static_assert(EPI == 0 || (BMT == 256 && BNT == 256 && BK == 64 && WM == 2 && WN == 4 && !SAVE),
+    static_assert(EPI == 0 || (BMT == 256 && BNT == 256 && BK == 64 && WM == 2 && WN == 4),
                   "staged epilogue shape");
     static_assert(!DYN || LDS_BYTES >= (3 * kMaxE + 1) * 4, "room for the tile list");
 
@@ -536,27 +536,56 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
             __syncthreads();                                // every wave is past the last K step
             const uint32_t rA = static_cast<uint32_t>(a_fill), rB = static_cast<uint32_t>(B_RING + b_fill);
             if constexpr (FC1) {
-                // tile row tr (256 bytes: 16 chunks, swizzled by row) of the
-                // staged activation tile; 16 lanes then write each row whole
+                // tile row tr (256 bytes: 16 chunks, swizzled by row) of a
+                // staged 256 x 128 tile; 16 lanes then write each row whole.
+                // Rounds: the activation, then (SAVE) the raw gate and up
+                // columns of the same rows, at col and I + col of preact.
                 auto so = [&](int tr, int c) {
                     const int rr = tr & 127;
                     return (tr < 128 ? rA : rB) + static_cast<uint32_t>(rr * 256 + ((c ^ (rr & 15)) << 4));
                 };
+                // raw gate (part 0: acc[0..7]) or up (part 1: acc[8..15])
+                // columns of block (mi, ni) as 8 bf16, like fc1_act's
+                auto fc1_raw = [&](int mi, int ni, int part) {
+                    const floatx16& v = acc[mi][ni];
+                    uint32_t x[2], y[2];
 #pragma unroll
-                for (int mi = 0; mi < MI; ++mi)
+                    for (int q = 0; q < 2; ++q) {
+                        x[q] = pack_bf16x2(v[8 * part + 2 * q], v[8 * part + 2 * q + 1]);
+                        y[q] = pack_bf16x2(v[8 * part + 2 * q + 4], v[8 * part + 2 * q + 5]);
+                    }
+                    const auto s0 = __builtin_amdgcn_permlane32_swap(x[0], y[0], false, false);
+                    const auto s1 = __builtin_amdgcn_permlane32_swap(x[1], y[1], false, false);
+                    u32x4 d;
+                    d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
+                    return d;
+                };
 #pragma unroll
-                    for (int ni = 0; ni < NI; ++ni)
-                        *(lds_u32x4*)((lds_u8*)smem + so(wm * WTM + mi * 32 + (lane & 31),
-                                                         ((wn * WTN + ni * 32) / 2 + 8 * half) / 8)) = fc1_act(mi, ni);
-                __syncthreads();
+                for (int round = 0; round < (SAVE ? 3 : 1); ++round) {
+                    if (round > 0) __syncthreads();        // the previous round is read back
 #pragma unroll
-                for (int j = 0; j < BMT / NW / 4; ++j) {
-                    const int tr = wave * (BMT / NW) + j * 4 + lane / 16, c = lane % 16;
-                    const u32x4 v = *(const lds_u32x4*)((lds_u8*)smem + so(tr, c));
-                    const int row = cur.m0 + tr, col = cur.nt * OUT_COLS + c * 8;
-                    const uint32_t off = row < cur.len && col < p.ncols
-                        ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob;
-                    __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, off, 0, POLICY);
+                    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                        for (int ni = 0; ni < NI; ++ni)
+                            *(lds_u32x4*)((lds_u8*)smem + so(wm * WTM + mi * 32 + (lane & 31),
+                                                             ((wn * WTN + ni * 32) / 2 + 8 * half) / 8)) =
+                                round == 0 ? fc1_act(mi, ni) : fc1_raw(mi, ni, round - 1);
+                    __syncthreads();
+#pragma unroll
+                    for (int j = 0; j < BMT / NW / 4; ++j) {
+                        const int tr = wave * (BMT / NW) + j * 4 + lane / 16, c = lane % 16;
+                        const u32x4 v = *(const lds_u32x4*)((lds_u8*)smem + so(tr, c));
+                        const int row = cur.m0 + tr, col = cur.nt * OUT_COLS + c * 8;
+                        const bool live = row < cur.len && col < p.ncols;
+                        if (round == 0) {
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                v, orsrc, live ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob, 0, POLICY);
+                        } else {
+                            const uint32_t poff = (static_cast<uint32_t>(row) * 2u * p.ncols + col +
+                                                   (round - 1) * static_cast<uint32_t>(p.ncols)) * 2u;
+                            __builtin_amdgcn_raw_buffer_store_b128(v, prsrc, live ? poff : kOob, 0, POLICY);
+                        }
+                    }
                 }
             } else {
                 // the wave's 8 KB, 64 rows of 128 bytes (its 64 columns, 8
@@ -695,7 +724,7 @@ int launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s, bool dyn = false) {
         // cost), FC2's route_out with the default policy (the combine reads
         // it next, partly from cache)
         constexpr bool STAGED = BMT == 256 && BNT == 256 && BK == 64 && WM == 2 && WN == 4;
-        if (fc1 && a.preact) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false, true>(a, s);
+        if (fc1 && a.preact) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false, true, STAGED ? 2 : 0>(a, s);
         else if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false, false, STAGED ? 2 : 0>(a, s);
         else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, false, false, STAGED ? 1 : 0>(a, s);
     }

@@ -170,6 +170,9 @@ __global__ __launch_bounds__(768) void slot_gemm_kernel(SlotArgs p) {
             b_fill = b_fill + B_STAGE == NB * B_STAGE ? 0 : b_fill + B_STAGE;
             wait_vmcnt<B_INST>();                  // slab g+1 is in: A(g+1) and the older B(g+1)
             __syncthreads();
+            // a tile ends at step g: the consumers stage its output in the
+            // two stages step g read, which stay unfilled until they are done
+            if ((g + 1) % KT == 0) __syncthreads();
         }
         wait_vmcnt<0>();   // no DMA may still be writing LDS when the workgroup ends
         return;
@@ -186,17 +189,21 @@ __global__ __launch_bounds__(768) void slot_gemm_kernel(SlotArgs p) {
             for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
     __syncthreads();
     int tc = t0, ktc = 0, a_rd = 0, b_rd = 0;
-    int orow[MI];                                  // ROWMAP: the output rows of the lane's slots
+    // ROWMAP: the output rows of the slots whose staged rows the lane writes
+    // (rows h*64 + j*8 + lane/8 of the wave's piece), fetched at the tile's
+    // first step and used at its end
+    int orow[ROWMAP ? MI / 2 * 8 : 1];
     for (int g = 0; g < S; ++g) {
         if (ROWMAP && ktc == 0) {
-            // fetched at the tile's first step, used at its end
             const int rest = tc / p.NT;
             const int e = rest / p.MT, m0 = (rest % p.MT) * BMT;
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi) {
-                const int row = m0 + wm * WTM + mi * 32 + (lane & 31);
-                orow[mi] = row < len ? p.out_rows[static_cast<int64_t>(e) * p.Cp + row] : -1;
-            }
+            for (int h = 0; h < MI / 2; ++h)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int slot = m0 + wm * WTM + h * 64 + j * 8 + lane / 8;
+                    orow[h * 8 + j] = slot < len ? p.out_rows[static_cast<int64_t>(e) * p.Cp + slot] : -1;
+                }
         }
         const uint8_t* sA = smem + a_rd;
         const lds_u8* sB = (const lds_u8*)smem + B_RING + b_rd;
@@ -221,13 +228,19 @@ __global__ __launch_bounds__(768) void slot_gemm_kernel(SlotArgs p) {
                 for (int ni = 0; ni < NI; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
         }
+        const int a_done = a_rd, b_done = b_rd;   // the stages this step read
         a_rd = a_rd == 0 ? A_STAGE : 0;
         b_rd = b_rd + B_STAGE == NB * B_STAGE ? 0 : b_rd + B_STAGE;
         if (++ktc == KT) {
             // the tile is done: lane (row l&31, half h) holds columns
             // 8g + 4h + (0..3) of each 32-column block in acc[4g..4g+3];
             // packed to bf16, a swap of lane halves gives each lane 8
-            // consecutive columns.  Rows past Cp and columns past Nn get an
+            // consecutive columns.  After a barrier (every consumer is past
+            // this step's LDS reads) each consumer stages its 128 x 64 piece,
+            // 64 rows at a time, in its own 8 KB of the two stages this step
+            // read (16-byte chunks swizzled by row) and writes each row's 128
+            // bytes with 8 lanes; the producers refill those stages only
+            // after the next barrier.  Rows past Cp and columns past Nn get an
             // offset beyond the descriptor: the store is dropped.
             const int nt = tc % p.NT, rest = tc / p.NT;
             const int e = rest / p.MT, m0 = (rest % p.MT) * BMT;
@@ -237,35 +250,62 @@ __global__ __launch_bounds__(768) void slot_gemm_kernel(SlotArgs p) {
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
                 ROWMAP ? p.out : p.out + static_cast<int64_t>(e) * p.Cp * p.ldo, static_cast<short>(0),
                 (ROWMAP ? rows_out : len) * p.ldo * 2, kRsrcWord3);
+            typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+            static_assert(NC == 8 && WTN == 64 && MI % 2 == 0 && A_STAGE >= 4 * 8192 && B_STAGE >= 4 * 8192,
+                          "staging: 8 KB per consumer in the stages a step reads");
+            __syncthreads();
+            lds_u8* st = (lds_u8*)smem + (wave < NC / 2 ? a_done + wave * 8192 : B_RING + b_done + (wave - NC / 2) * 8192);
+            auto so = [](int r, int c) { return static_cast<uint32_t>(r * 128 + ((c ^ (r & 7)) << 4)); };
 #pragma unroll
-            for (int mi = 0; mi < MI; ++mi) {
-                // the lane's output row: its slot within the segment, or the
-                // mapped row of the whole output (live if inside it)
-                const int row = ROWMAP ? orow[mi] : m0 + wm * WTM + mi * 32 + (lane & 31);
-                const bool row_live = ROWMAP ? static_cast<unsigned>(row) < static_cast<unsigned>(rows_out)
-                                             : row < len;
+            for (int h = 0; h < MI / 2; ++h) {
+                asm volatile("" ::: "memory");
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni) {
-                    uint32_t gq[4][2];
+                for (int m2 = 0; m2 < 2; ++m2) {
+                    const int mi = 2 * h + m2;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        gq[q][0] = pack_bf16x2(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1]);
-                        gq[q][1] = pack_bf16x2(acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
+                    for (int ni = 0; ni < NI; ++ni) {
+                        uint32_t gq[4][2];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            gq[q][0] = pack_bf16x2(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1]);
+                            gq[q][1] = pack_bf16x2(acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
+                        }
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const auto s0 = __builtin_amdgcn_permlane32_swap(gq[2 * q][0], gq[2 * q + 1][0], false, false);
+                            const auto s1 = __builtin_amdgcn_permlane32_swap(gq[2 * q][1], gq[2 * q + 1][1], false, false);
+                            u32x4 d;
+                            d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
+                            *(lds_u32x4*)(st + so(m2 * 32 + (lane & 31), ni * 4 + 2 * q + half)) = d;
+                        }
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
                     }
-#pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const auto s0 = __builtin_amdgcn_permlane32_swap(gq[2 * q][0], gq[2 * q + 1][0], false, false);
-                        const auto s1 = __builtin_amdgcn_permlane32_swap(gq[2 * q][1], gq[2 * q + 1][1], false, false);
-                        u32x4 d;
-                        d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
-                        const int col = nt * BNT + wn * WTN + ni * 32 + 16 * q + 8 * half;
-                        const uint32_t off = row_live && col < p.Nn
-                            ? (static_cast<uint32_t>(row) * p.ldo + col) * 2u : kOob;
-                        __builtin_amdgcn_raw_buffer_store_b128(d, orsrc, off, 0, 0);
-                    }
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
                 }
+                // the wave reads back what its other lanes wrote: LDS
+                // operations of one wave complete in order, and the clobbers
+                // keep the compiler from moving them across
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int r = j * 8 + lane / 8, c = lane % 8;
+                    const u32x4 v = *(const lds_u32x4*)(st + so(r, c));
+                    const int srow = h * 64 + r;                      // row of the wave's piece
+                    int row;
+                    bool row_live;
+                    if (ROWMAP) {
+                        row = orow[ROWMAP ? h * 8 + j : 0];       // slot m0 + wm*WTM + srow's
+                        row_live = static_cast<unsigned>(row) < static_cast<unsigned>(rows_out);
+                    } else {
+                        row = m0 + wm * WTM + srow;
+                        row_live = row < len;
+                    }
+                    const int col = nt * BNT + wn * WTN + c * 8;
+                    const uint32_t off = row_live && col < p.Nn
+                        ? (static_cast<uint32_t>(row) * p.ldo + col) * 2u : kOob;
+                    __builtin_amdgcn_raw_buffer_store_b128(v, orsrc, off, 0, 0);
+                }
+                asm volatile("" ::: "memory");
             }
             ktc = 0;
             tc += G;

@@ -120,9 +120,11 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
     static_assert(LDS_BYTES <= 160 * 1024, "LDS");
     // Staged epilogue (EPI 1: default store policy, 2: non-temporal): the
     // tile leaves through the A and B stages its last K step freed.  FC1
-    // stages the whole 256 x 128 activation tile (A stage rows 0-127, B stage
-    // rows 128-255); FC2 gives each wave 8 KB of them for its 128 x 64 piece.
-    static_assert(EPI == 0 || (BMT == 256 && BNT == 256 && BK == 64 && WM == 2 && WN == 4),
+    // stages its 128-column tile as many rows at a time as they hold (all
+    // 256 rows of a 256-row tile; 288 then 32 of a 320-row one, though the
+    // launcher keeps that shape on direct stores); FC2 gives each wave 8 KB
+    // of them for its piece, 64 rows at a time.
+    static_assert(EPI == 0 || ((BMT == 256 || BMT == 320) && BNT == 256 && BK == 64 && WM == 2 && WN == 4),
                   "staged epilogue shape");
     static_assert(!DYN || LDS_BYTES >= (3 * kMaxE + 1) * 4, "room for the tile list");
 
@@ -536,13 +538,17 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
             __syncthreads();                                // every wave is past the last K step
             const uint32_t rA = static_cast<uint32_t>(a_fill), rB = static_cast<uint32_t>(B_RING + b_fill);
             if constexpr (FC1) {
-                // tile row tr (256 bytes: 16 chunks, swizzled by row) of a
-                // staged 256 x 128 tile; 16 lanes then write each row whole.
-                // Rounds: the activation, then (SAVE) the raw gate and up
-                // columns of the same rows, at col and I + col of preact.
-                auto so = [&](int tr, int c) {
-                    const int rr = tr & 127;
-                    return (tr < 128 ? rA : rB) + static_cast<uint32_t>(rr * 256 + ((c ^ (rr & 15)) << 4));
+                // The freed A and B stages hold CAP rows of 256 bytes (16
+                // chunks, swizzled by row) of a 128-column tile: rows
+                // [base, base + CAP) of the tile go there per round, then 16
+                // lanes write each row whole.  Parts: the activation, then
+                // (SAVE) the raw gate and up columns of the same rows, at col
+                // and I + col of preact.
+                constexpr int ROWS_A = A_STAGE / 256, CAP = ROWS_A + B_STAGE / 256;
+                static_assert(OUT_COLS == 128 && CAP % 32 == 0, "staged FC1 rows");
+                auto so = [&](int sr, int c) {
+                    const int rr = sr < ROWS_A ? sr : sr - ROWS_A;
+                    return (sr < ROWS_A ? rA : rB) + static_cast<uint32_t>(rr * 256 + ((c ^ (rr & 15)) << 4));
                 };
                 // raw gate (part 0: acc[0..7]) or up (part 1: acc[8..15])
                 // columns of block (mi, ni) as 8 bf16, like fc1_act's
@@ -560,55 +566,72 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
                     d[0] = s0[0]; d[1] = s1[0]; d[2] = s0[1]; d[3] = s1[1];
                     return d;
                 };
+                bool started = false;
 #pragma unroll
-                for (int round = 0; round < (SAVE ? 3 : 1); ++round) {
-                    if (round > 0) __syncthreads();        // the previous round is read back
+                for (int part = 0; part < (SAVE ? 3 : 1); ++part) {
 #pragma unroll
-                    for (int mi = 0; mi < MI; ++mi)
+                    for (int base = 0; base < BMT; base += CAP) {
+                        if (started) __syncthreads();      // the previous round is read back
+                        started = true;
 #pragma unroll
-                        for (int ni = 0; ni < NI; ++ni)
-                            *(lds_u32x4*)((lds_u8*)smem + so(wm * WTM + mi * 32 + (lane & 31),
-                                                             ((wn * WTN + ni * 32) / 2 + 8 * half) / 8)) =
-                                round == 0 ? fc1_act(mi, ni) : fc1_raw(mi, ni, round - 1);
-                    __syncthreads();
+                        for (int mi = 0; mi < MI; ++mi) {
+                            const int r0 = wm * WTM + mi * 32;   // the block's first tile row
+                            if (r0 < base || r0 >= base + CAP) continue;
 #pragma unroll
-                    for (int j = 0; j < BMT / NW / 4; ++j) {
-                        const int tr = wave * (BMT / NW) + j * 4 + lane / 16, c = lane % 16;
-                        const u32x4 v = *(const lds_u32x4*)((lds_u8*)smem + so(tr, c));
-                        const int row = cur.m0 + tr, col = cur.nt * OUT_COLS + c * 8;
-                        const bool live = row < cur.len && col < p.ncols;
-                        if (round == 0) {
-                            __builtin_amdgcn_raw_buffer_store_b128(
-                                v, orsrc, live ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob, 0, POLICY);
-                        } else {
-                            const uint32_t poff = (static_cast<uint32_t>(row) * 2u * p.ncols + col +
-                                                   (round - 1) * static_cast<uint32_t>(p.ncols)) * 2u;
-                            __builtin_amdgcn_raw_buffer_store_b128(v, prsrc, live ? poff : kOob, 0, POLICY);
+                            for (int ni = 0; ni < NI; ++ni)
+                                *(lds_u32x4*)((lds_u8*)smem + so(r0 - base + (lane & 31),
+                                                                 ((wn * WTN + ni * 32) / 2 + 8 * half) / 8)) =
+                                    part == 0 ? fc1_act(mi, ni) : fc1_raw(mi, ni, part - 1);
+                        }
+                        __syncthreads();
+                        const int cnt = BMT - base < CAP ? BMT - base : CAP;   // rows this round
+#pragma unroll
+                        for (int j = 0; j < (CAP + NW * 4 - 1) / (NW * 4); ++j) {
+                            const int sr = j * NW * 4 + wave * 4 + lane / 16, c = lane % 16;
+                            if (j * NW * 4 >= cnt) break;            // uniform: whole instructions
+                            const u32x4 v = *(const lds_u32x4*)((lds_u8*)smem + so(sr, c));
+                            const int row = cur.m0 + base + sr, col = cur.nt * OUT_COLS + c * 8;
+                            const bool live = sr < cnt && row < cur.len && col < p.ncols;
+                            if (part == 0) {
+                                __builtin_amdgcn_raw_buffer_store_b128(
+                                    v, orsrc, live ? (static_cast<uint32_t>(row) * p.ncols + col) * 2u : kOob, 0, POLICY);
+                            } else {
+                                const uint32_t poff = (static_cast<uint32_t>(row) * 2u * p.ncols + col +
+                                                       (part - 1) * static_cast<uint32_t>(p.ncols)) * 2u;
+                                __builtin_amdgcn_raw_buffer_store_b128(v, prsrc, live ? poff : kOob, 0, POLICY);
+                            }
                         }
                     }
                 }
             } else {
-                // the wave's 8 KB, 64 rows of 128 bytes (its 64 columns, 8
-                // chunks swizzled by row) per round, two row blocks a round;
+                // each wave gets 8 KB of the freed stages (slots that do not
+                // straddle them) for its WTM x 64 piece, 64 rows (two row
+                // blocks) of 128 bytes (8 chunks swizzled by row) per round;
                 // the wave reads back what its other lanes wrote (LDS
                 // operations of one wave complete in order; the clobbers keep
-                // the compiler from moving them across)
-                const uint32_t base = wave < NW / 2 ? rA + wave * 8192u : rB + (wave - NW / 2) * 8192u;
+                // the compiler from moving them across), 8 lanes per line
+                constexpr int SLOTS_A = A_STAGE / 8192;
+                static_assert(WTN == 64 && SLOTS_A + B_STAGE / 8192 >= NW, "staged FC2 slots");
+                const uint32_t base = wave < SLOTS_A ? rA + wave * 8192u : rB + (wave - SLOTS_A) * 8192u;
                 auto so = [&](int r, int c) { return base + static_cast<uint32_t>(r * 128 + ((c ^ (r & 7)) << 4)); };
 #pragma unroll
-                for (int h = 0; h < MI / 2; ++h) {
+                for (int h = 0; h < (MI + 1) / 2; ++h) {
                     asm volatile("" ::: "memory");
 #pragma unroll
-                    for (int m2 = 0; m2 < 2; ++m2)
+                    for (int m2 = 0; m2 < 2; ++m2) {
+                        if (2 * h + m2 >= MI) continue;
 #pragma unroll
                         for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
                             for (int q = 0; q < 2; ++q)
                                 *(lds_u32x4*)((lds_u8*)smem + so(m2 * 32 + (lane & 31), ni * 4 + 2 * q + half)) =
                                     fc2_out(2 * h + m2, ni, q);
+                    }
                     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                    const int nrows = 2 * h + 1 < MI ? 64 : 32;
 #pragma unroll
                     for (int j = 0; j < 8; ++j) {
+                        if (j * 8 >= nrows) break;
                         const int r = j * 8 + lane / 8, c = lane % 8;
                         const u32x4 v = *(const lds_u32x4*)((lds_u8*)smem + so(r, c));
                         const int row = cur.m0 + wm * WTM + h * 64 + r, col = cur.nt * OUT_COLS + wn * WTN + c * 8;
@@ -715,18 +738,21 @@ int launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s, bool dyn = false) {
     a.NT = fc1 ? (a.ncols + BNT / 2 - 1) / (BNT / 2) : (a.ncols + BNT - 1) / BNT;
     a.tiles = E * a.MT * a.NT;
     a.E = E;
+    // Tiles of 256 x 256 (FC1 and FC2) and 320 x 256 (FC2) leave through the
+    // staged epilogue: FC1's activation non-temporal (FC2 reads it from HBM
+    // at no measured cost), FC2's route_out with the default policy (the
+    // combine reads it next, partly from cache).  A 320-row FC1 tile keeps
+    // direct stores: staged, its registers spill (280 vs 233 us).
+    constexpr bool SHAPE = BNT == 256 && BK == 64 && WM == 2 && WN == 4;
+    constexpr bool STAGED = SHAPE && BMT == 256;
+    constexpr bool STAGED2 = SHAPE && (BMT == 256 || BMT == 320);
     if (dyn) {
-        if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, true>(a, s);
-        else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, true>(a, s);
+        if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, true, false, STAGED ? 2 : 0>(a, s);
+        else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, true, false, STAGED2 ? 1 : 0>(a, s);
     } else {
-        // 256 x 256 tiles leave through the staged epilogue: FC1's
-        // activation non-temporal (FC2 reads it from HBM at no measured
-        // cost), FC2's route_out with the default policy (the combine reads
-        // it next, partly from cache)
-        constexpr bool STAGED = BMT == 256 && BNT == 256 && BK == 64 && WM == 2 && WN == 4;
         if (fc1 && a.preact) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false, true, STAGED ? 2 : 0>(a, s);
         else if (fc1) launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, true, false, false, STAGED ? 2 : 0>(a, s);
-        else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, false, false, STAGED ? 1 : 0>(a, s);
+        else launch_persistent<BMT, BNT, WM, WN, BK, NA, NB, false, false, false, STAGED2 ? 1 : 0>(a, s);
     }
     return MOE_OK;
 }

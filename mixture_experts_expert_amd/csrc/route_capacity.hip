@@ -559,13 +559,16 @@ template <int T>
 void launch_select_t(const RouteMap& rm, int N, int E, int K, int C, int* route_slot,
                      int* expert_count, const AlignOut& ao, hipStream_t s) {
     const size_t lds = select_lds_bytes(N);
-    static std::atomic<bool> raised{false};
-    if (lds > 64 * 1024 && !raised.load(std::memory_order_relaxed)) {
-        // past 64 KB of dynamic LDS the launch needs the kernel's limit raised
+    // past 64 KB of dynamic LDS the launch needs the kernel's limit raised,
+    // once per device (the attribute belongs to the device the call runs on)
+    static std::atomic<bool> raised[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+    if (lds > 64 * 1024 && (dev >= 64 || !raised[dev].load(std::memory_order_relaxed))) {
         (void)hipFuncSetAttribute(reinterpret_cast<const void*>(capacity_select_kernel<T>),
                                   hipFuncAttributeMaxDynamicSharedMemorySize,
                                   static_cast<int>(select_lds_bytes(static_cast<int>(kMaxN))));
-        raised.store(true, std::memory_order_relaxed);
+        if (dev < 64) raised[dev].store(true, std::memory_order_relaxed);
     }
     capacity_select_kernel<T><<<E, T, lds, s>>>(rm.picks, rm.probs, rm.Np, N, K, C, route_slot,
                                                 expert_count, ao);

@@ -69,7 +69,8 @@ def test_dropless_workload_parity(name, skew_alpha):
 
 @pytest.mark.parametrize("case", ["single_token", "ragged_n77_h192_i320", "tied_integer_logits",
                                   "overload_one_expert", "wide_e1000_k32", "e100_k7_f2",
-                                  "max_tokens_all_to_one"])
+                                  "max_tokens_all_to_one", "dyn_256_tiles_n1000_h256_i192",
+                                  "dyn_hot_rows_n1000_h256_i192"])
 def test_dropless_edge_case_parity(case):
     s, mode = EDGE[case]
     say(f"[dropless edge] {case}")

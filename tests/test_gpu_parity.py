@@ -102,6 +102,11 @@ EDGE = {
     # with two row tiles per expert
     "whole_tiles_ragged_h320_i192": (Shape(512, 320, 192, 8, 4, 1.0), None),
     "two_row_tiles_c512": (Shape(1024, 256, 128, 8, 4, 1.0), None),
+    # in the dropless form a mean of 125 routes per expert takes 256-row tiles
+    # (the staged epilogue); "hot" puts every token on expert 0, whose
+    # 1000-route segment then spans four row tiles, the last one partial
+    "dyn_256_tiles_n1000_h256_i192": (Shape(1000, 256, 192, 8, 1, 1.0), None),
+    "dyn_hot_rows_n1000_h256_i192": (Shape(1000, 256, 192, 8, 1, 1.0), "hot"),
 }
 
 

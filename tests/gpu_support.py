@@ -122,10 +122,12 @@ def grad_vals(v):
     return oracle.bf16_bits_to_f64(v) if v.dtype == np.uint16 else v.astype(np.float64)
 
 
-def assert_grad_close(gpu, ref, what, rtol=RTOL, atol_rms=ATOL_RMS, norm_tol=NORM_TOL, terms=None):
+def assert_grad_close(gpu, ref, what, rtol=RTOL, atol_rms=ATOL_RMS, norm_tol=NORM_TOL, terms=None,
+                      quiet=False):
     """terms: for a result that sums separately rounded bf16 values, the
     elementwise sum of their magnitudes; one ulp (2^-8 relative) may flip in
-    each of them, so 2^-7 * terms joins the bar."""
+    each of them, so 2^-7 * terms joins the bar.  Returns the normwise
+    relative error (quiet: without printing it)."""
     g, r = grad_vals(gpu), grad_vals(ref)
     assert g.shape == r.shape, (what, g.shape, r.shape)
     rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
@@ -135,7 +137,9 @@ def assert_grad_close(gpu, ref, what, rtol=RTOL, atol_rms=ATOL_RMS, norm_tol=NOR
         bar = bar + 2.0 ** -7 * terms
     bad = d > bar
     nr = float(np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30))
-    say(f"  {what}: normwise rel err {nr:.2e}, max abs err {d.max(initial=0):.2e} "
-        f"(rms {rms:.2e}), exact {float(np.mean(g == r)) if g.size else 1.0:.4f}")
+    if not quiet:
+        say(f"  {what}: normwise rel err {nr:.2e}, max abs err {d.max(initial=0):.2e} "
+            f"(rms {rms:.2e}), exact {float(np.mean(g == r)) if g.size else 1.0:.4f}")
     assert not bad.any(), f"{what}: {int(bad.sum())} elements outside the bar"
     assert nr <= norm_tol, f"{what}: normwise relative error {nr:.3e}"
+    return nr

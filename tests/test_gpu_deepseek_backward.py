@@ -2,13 +2,13 @@
 H=7168, E=256, K=8, F=1.0, I=2048), full size, in the launch configuration
 the benchmark times (forward keeping the pre-activation, then the backward).
 
-The float64 oracle over all 256 experts would take many minutes, so the
-GEMM steps are checked step-wise on sampled experts (the oracle's step
-functions over one expert's segment, fed the GPU's own inputs to each step):
-the pre-activation, FC2 dgrad, the SwiGLU backward, FC1 dgrad and both
-weight gradients of each sampled expert in full.  The dx gather-combine
-(bit-exact) and the router-logit gradient are checked over every token.
-Bars are the backward's (tests/test_gpu_backward.py).
+The GEMM steps are checked step-wise on every expert (the oracle's step
+functions over one expert's segment, fed the GPU's own inputs to each step,
+that expert's weights copied to the host): the pre-activation, FC2 dgrad, the
+SwiGLU backward, FC1 dgrad and both weight gradients, every element, pads
+included, in eight chunks of experts so that no single test runs long.  The
+dx gather-combine (bit-exact) and the router-logit gradient are checked over
+every token.  Bars are the backward's (tests/test_gpu_backward.py).
 """
 
 import numpy as np
@@ -41,41 +41,51 @@ def run():
     return T, dy, buf, bw, m
 
 
-def _sampled_experts(m, Cp):
-    """The expert with the most pad slots (pad rows must stay zero) and two
-    seeded others."""
-    ssi = m["sorted_slot_ids"]
-    pads = (ssi.reshape(W.E, Cp) == W.N).sum(axis=1)
-    rng = np.random.default_rng(11)
-    picks = {int(np.argmax(pads))} | set(rng.choice(W.E, size=2, replace=False).tolist())
-    return sorted(picks)
+CHUNKS = 8                     # expert chunks of the full GEMM-step check
 
 
-def test_gemm_steps_on_sampled_experts(run):
+@pytest.fixture(scope="module")
+def host_state(run):
+    T, dy, buf, bw, m = run
+    return {"x": host(T["x"]), "dy": host(dy)}
+
+
+@pytest.mark.parametrize("chunk", range(CHUNKS))
+def test_gemm_steps_every_expert(run, host_state, chunk):
     T, dy, buf, bw, m = run
     Cp = buf.Cp
     ssi, sp = m["sorted_slot_ids"], m["slot_probs"]
-    x, dyb = host(T["x"]), host(dy)
-    for e in _sampled_experts(m, Cp):
+    x, dyb = host_state["x"], host_state["dy"]
+    per = W.E // CHUNKS
+    experts = range(chunk * per, (chunk + 1) * per)
+    worst = {}
+    for e in experts:
         seg = slice(e * Cp, (e + 1) * Cp)
         ssi_e, sp_e = ssi[seg], sp[seg]
         w1_e, w2_e = host(T["w1"][e:e + 1]), host(T["w2"][e:e + 1])
         pads = ssi_e == W.N
-        say(f"  expert {e}: {int((~pads).sum())} routed slots, {int(pads.sum())} pads")
         g_pre, g_dact, g_act = host(bw.preact[seg]), host(bw.d_act[seg]), host(bw.act_re[seg])
         g_dpre, g_dprob, g_da = host(bw.d_preact[seg]), host(bw.d_prob[seg]), host(bw.d_a[seg])
-        assert_grad_close(g_pre, oracle.fc1_preact_slots(x, w1_e, ssi_e, 1, Cp), f"preact e{e}")
-        assert_grad_close(g_dact, oracle.fc2_dgrad(dyb, w2_e, ssi_e, 1, Cp), f"d_act e{e}")
+        checks = [
+            (g_pre, oracle.fc1_preact_slots(x, w1_e, ssi_e, 1, Cp), "preact", {}),
+            (g_dact, oracle.fc2_dgrad(dyb, w2_e, ssi_e, 1, Cp), "d_act", {}),
+        ]
         r_act, r_dpre, r_dprob = oracle.swiglu_backward(g_pre, g_dact, sp_e)
-        assert_grad_close(g_act, r_act, f"act recomputed e{e}")
-        assert_grad_close(g_dpre, r_dpre, f"d_preact e{e}")
-        assert_grad_close(g_dprob, r_dprob, f"d_prob e{e}", rtol=F32_TOL, atol_rms=F32_TOL, norm_tol=F32_TOL)
-        assert_grad_close(g_da, oracle.fc1_dgrad(g_dpre, w1_e, 1, Cp), f"d_a e{e}")
-        assert_grad_close(host(bw.dw2[e]), oracle.fc2_wgrad(dyb, g_act, ssi_e, 1, Cp)[0], f"dW2[{e}]")
-        assert_grad_close(host(bw.dw1[e]), oracle.fc1_wgrad(g_dpre, x, ssi_e, 1, Cp)[0], f"dW1[{e}]")
+        checks += [
+            (g_act, r_act, "act recomputed", {}),
+            (g_dpre, r_dpre, "d_preact", {}),
+            (g_dprob, r_dprob, "d_prob", dict(rtol=F32_TOL, atol_rms=F32_TOL, norm_tol=F32_TOL)),
+            (g_da, oracle.fc1_dgrad(g_dpre, w1_e, 1, Cp), "d_a", {}),
+            (host(bw.dw2[e]), oracle.fc2_wgrad(dyb, g_act, ssi_e, 1, Cp)[0], "dW2", {}),
+            (host(bw.dw1[e]), oracle.fc1_wgrad(g_dpre, x, ssi_e, 1, Cp)[0], "dW1", {}),
+        ]
+        for g, r, name, kw in checks:
+            worst[name] = max(worst.get(name, 0.0), assert_grad_close(g, r, f"{name} e{e}", quiet=True, **kw))
         for name, v in (("d_act", g_dact), ("act", g_act), ("d_preact", g_dpre), ("d_a", g_da)):
             assert np.all(v[pads] == 0), f"{name} e{e}: pad rows must be zero"
         assert np.all(g_dprob[pads] == 0)
+    say(f"  experts {experts.start}..{experts.stop - 1}: every GEMM step checked; worst normwise "
+        + ", ".join(f"{k} {v:.1e}" for k, v in worst.items()))
 
 
 def test_dx_and_router_gradient_all_tokens(run):

@@ -7,8 +7,8 @@ offsets allow.
 
 * a small layer with N > 16384 rows, every slot checked against the oracle;
 * the Qwen3-30B-A3B shape at ep = 8 (16 local experts, 2048 rows each, the
-  configuration `bench.py --variant ep-local` times): two experts checked in
-  full and four sampled rows of every other expert.
+  configuration `bench.py --variant ep-local` times): every row of every
+  expert.
 
 Bars: the forward's (act and route_out within 1e-2 + 2e-2|ref| and normwise
 1e-2), oracle.expert_ffn / oracle.grouped_ffn on the same rows.
@@ -59,15 +59,12 @@ def test_qwen_shape_ep8_share():
     _, act, ro = _run(d)
     E = d["E"]
     say(f"  {E} local experts x {C} rows = {E * C} rows")
-    x, pr = host(d["x"]), host(d["probs"])
-    rng = np.random.default_rng(3)
-    full = set(rng.choice(E, size=2, replace=False).tolist())
+    x, pr, g_act, g_ro = host(d["x"]), host(d["probs"]), host(act), host(ro)
     for e in range(E):
-        rows = np.arange(e * C, (e + 1) * C) if e in full else np.sort(rng.choice(np.arange(e * C, (e + 1) * C), 4, replace=False))
+        rows = slice(e * C, (e + 1) * C)
         r_act, r_out = oracle.expert_ffn(x[rows], host(d["w1"][e]), host(d["w2"][e]), pr[rows])
-        idx = torch.as_tensor(rows, device="cuda")
-        assert_bf16_close(host(act[idx]), r_act, f"act e{e}")
-        assert_bf16_close(host(ro[idx]), r_out, f"route_out e{e}")
+        assert_bf16_close(g_act[rows], r_act, f"act e{e}")
+        assert_bf16_close(g_ro[rows], r_out, f"route_out e{e}")
 
 
 def test_source_major_receive_buffer():

@@ -225,6 +225,49 @@ def hbm_probes(torch, moe, stream, nbytes=2 << 30, reps=10):
     return out
 
 
+def access_order_probes(torch, moe, w, reps=10):
+    """GB/s of the library's access-order probes over a buffer the size of
+    the workload's W1 ([E, 2I, H] bf16, as panels of 256 rows of H*2 bytes):
+    reads and writes in the order a GEMM tile walks a weight panel (pieces of
+    128, 256 or 512 bytes of every row in turn) against front to back, and the
+    GEMMs' LDS-DMA ring alone at 2-5 stages.  Prints one JSON line."""
+    row = w.H * 2
+    panel = 256 * row
+    nbytes = (w.E * 2 * w.I * w.H * 2) // panel * panel
+    nbytes -= nbytes % (1 << 20)
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    pieces = [p for p in (128, 256, 512) if row % p == 0] + [row]
+
+    def rate(fn):
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                fn()
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(reps):
+                fn()
+            ev1.record(stream)
+            stream.synchronize()
+        return nbytes * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+
+    out = {"probe": "access_order", "workload": w.name, "buffer_bytes": nbytes, "row_bytes": row,
+           "rows_per_panel": 256, "reps": reps,
+           "read_gbs": {}, "write_gbs": {"nontemporal": {}, "default": {}}, "lds_ring_gbs": {}}
+    moe.moe_probe_write(buf, stream)
+    for p in pieces:
+        key = "front_to_back" if p == row else str(p)
+        out["read_gbs"][key] = rate(lambda: moe.moe_probe_read_pieces(buf, row, 256, p, sink, stream))
+        for nt in (True, False):
+            out["write_gbs"]["nontemporal" if nt else "default"][key] = rate(
+                lambda: moe.moe_probe_write_pieces(buf, row, 256, p, nt, stream))
+    for st in (2, 3, 4, 5):
+        out["lds_ring_gbs"][str(st)] = rate(lambda: moe.moe_probe_lds_ring(buf, st, sink, stream))
+    log("[bench] access-order probes GB/s: " + json.dumps({k: out[k] for k in ("read_gbs", "write_gbs", "lds_ring_gbs")}))
+    print(json.dumps(out))
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling the FETCH/WRITE counters."""
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
@@ -737,6 +780,9 @@ def main():
                          "FC1 and FC2 shapes, as context for the grouped kernels, and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--access-order-probes", action="store_true",
+                    help="only time the library's access-order and LDS-ring probes over a buffer "
+                         "the size of the workload's W1, print one JSON line and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -753,6 +799,9 @@ def main():
         return
 
     w = moe_inputs.WORKLOADS[args.workload or moe_inputs.HEADLINE]
+    if args.access_order_probes:
+        access_order_probes(torch, moe, w)
+        return
     if args.vendor_reference:
         vendor_reference(torch, moe, w, args)
         return

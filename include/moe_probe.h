@@ -4,7 +4,9 @@
  * layer: the benchmark times them to state, for this device, the HBM rate a
  * plain streaming read, a streaming write and a copy reach, and sets the
  * layer's kernels against those rates (the published 8 TB/s is a nominal
- * peak no access pattern reaches).
+ * peak no access pattern reaches); the access-order probes state what the
+ * order of a GEMM tile's weight reads and output writes, and the LDS-DMA
+ * ring the GEMMs load through, cost by themselves.
  *
  * Conventions: device pointers owned by the caller, 16-byte aligned, byte
  * counts multiples of 16 (MOE_ERR_MISALIGNED otherwise); a null pointer is
@@ -35,6 +37,36 @@ int moe_probe_write(void* dst, size_t bytes, hipStream_t stream);
 /* dst = src over `bytes` (non-temporal 16-byte loads and stores); the
  * buffers must not overlap. */
 int moe_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream);
+
+/* Access-order probes.  The buffer is a sequence of panels of `rows` rows of
+ * `row_bytes` bytes (`bytes` a whole number of panels); one 512-thread
+ * workgroup per compute unit walks whole panels, each piece column by piece
+ * column: bytes [s, s + piece_bytes) of every row, then the next s -- the
+ * order in which a GEMM tile streams a weight panel in K slabs (piece_bytes
+ * == row_bytes: front to back).  16-byte accesses, eight in flight per
+ * thread.  row_bytes and piece_bytes are multiples of 16 and piece_bytes
+ * divides row_bytes (MOE_ERR_MISALIGNED otherwise); rows >= 1, row_bytes
+ * and piece_bytes >= 16 and bytes a multiple of rows * row_bytes
+ * (MOE_ERR_INVALID_ARG otherwise); one panel below 2^35 bytes
+ * (MOE_ERR_UNSUPPORTED).
+ *
+ * moe_probe_read_pieces reads every byte once (non-temporal loads) and
+ * writes at most one word to sink[0] (its value means nothing);
+ * moe_probe_write_pieces writes every byte once with a fixed pattern,
+ * non-temporal stores when `nontemporal` is nonzero. */
+int moe_probe_read_pieces(const void* src, size_t bytes, int32_t row_bytes, int32_t rows,
+                          int32_t piece_bytes, uint32_t* sink, hipStream_t stream);
+int moe_probe_write_pieces(void* dst, size_t bytes, int32_t row_bytes, int32_t rows,
+                           int32_t piece_bytes, int32_t nontemporal, hipStream_t stream);
+
+/* The GEMMs' load pipeline without their compute: one 512-thread workgroup
+ * per compute unit streams contiguous 1 MiB panels of src in 32 KiB slabs
+ * through `stages` (2..5) LDS stages by LDS DMA (non-temporal), with a wait
+ * for the current slab and a workgroup barrier per slab.  `bytes` is a
+ * multiple of 1 MiB and stages in [2, 5] (MOE_ERR_INVALID_ARG otherwise);
+ * writes at most one word to sink[0]. */
+int moe_probe_lds_ring(const void* src, size_t bytes, int32_t stages, uint32_t* sink,
+                       hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -30,8 +30,11 @@ from ._native import (  # noqa: F401
     moe_layout_block_m,
     moe_padded_capacity,
     moe_probe_copy,
+    moe_probe_lds_ring,
     moe_probe_read,
+    moe_probe_read_pieces,
     moe_probe_write,
+    moe_probe_write_pieces,
     PROBE_HEADER_PATH,
     moe_route_bwd,
     moe_route_capacity,

@@ -78,6 +78,9 @@ _SIGNATURES = {
     "moe_probe_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _vp]),
     "moe_probe_write": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp]),
     "moe_probe_copy": (ctypes.c_int, [_vp, _vp, ctypes.c_size_t, _vp]),
+    "moe_probe_read_pieces": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _i32, _vp, _vp]),
+    "moe_probe_write_pieces": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _i32, _i32, _vp]),
+    "moe_probe_lds_ring": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -117,6 +120,31 @@ def moe_probe_copy(src, dst, stream=None):
     if n != m:
         raise ValueError("moe_probe_copy: src and dst differ in size")
     _check("moe_probe_copy", lib.moe_probe_copy(ps, pd, n, _stream(stream)))
+
+
+def moe_probe_read_pieces(src, row_bytes: int, rows: int, piece_bytes: int, sink, stream=None):
+    """Read src as panels of rows x row_bytes, piece column by piece column
+    (an access-order probe); sink: int32 device tensor."""
+    p, n = _bytes_ptr(src, "src")
+    _check("moe_probe_read_pieces", lib.moe_probe_read_pieces(
+        p, n, row_bytes, rows, piece_bytes, _bytes_ptr(sink, "sink")[0], _stream(stream)))
+
+
+def moe_probe_write_pieces(dst, row_bytes: int, rows: int, piece_bytes: int, nontemporal: bool,
+                           stream=None):
+    """Write dst as panels of rows x row_bytes, piece column by piece column
+    (an access-order probe)."""
+    p, n = _bytes_ptr(dst, "dst")
+    _check("moe_probe_write_pieces", lib.moe_probe_write_pieces(
+        p, n, row_bytes, rows, piece_bytes, int(bool(nontemporal)), _stream(stream)))
+
+
+def moe_probe_lds_ring(src, stages: int, sink, stream=None):
+    """Stream src (whole MiB) through an LDS-DMA ring of `stages` 32 KiB
+    stages (the GEMMs' load pipeline alone); sink: int32 device tensor."""
+    p, n = _bytes_ptr(src, "src")
+    _check("moe_probe_lds_ring", lib.moe_probe_lds_ring(p, n, stages, _bytes_ptr(sink, "sink")[0],
+                                                        _stream(stream)))
 
 
 class MoEError(RuntimeError):

@@ -11,7 +11,7 @@
 #include <algorithm>
 
 #include "../../include/moe_probe.h"
-#include "moe_common.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace {
@@ -80,6 +80,114 @@ __global__ __launch_bounds__(kProbeThreads) void probe_copy_kernel(const v4u* __
     for (; i < hi; i += kProbeThreads) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
 }
 
+// ---- access-order probes: one 512-thread workgroup per CU, each walking
+// whole panels (rows x row_words 16-byte words).  A panel is visited piece
+// column by piece column: words [s, s + piece_words) of every row, then the
+// next s -- the order in which a GEMM tile streams its weight panel in K
+// slabs (piece_words == row_words: front to back).  Eight 16-byte accesses
+// in flight per thread.
+constexpr int kPieceThreads = 512;
+
+// word w of piece column s of a panel, as an offset from the panel's start
+__device__ __forceinline__ size_t piece_word(int w, int s, int row_words, int piece_words) {
+    const int r = w / piece_words, c = w - r * piece_words;
+    return static_cast<size_t>(r) * row_words + s + c;
+}
+
+__global__ __launch_bounds__(kPieceThreads) void probe_read_pieces_kernel(
+    const v4u* __restrict__ src, size_t panels, int rows, int row_words, int piece_words,
+    uint32_t* __restrict__ sink) {
+    constexpr int U = 8;
+    const int col_words = rows * piece_words;
+    uint32_t acc = 0;
+    for (size_t p = blockIdx.x; p < panels; p += gridDim.x) {
+        const v4u* base = src + p * static_cast<size_t>(rows) * row_words;
+        for (int s = 0; s < row_words; s += piece_words) {
+            // U loads issued together per step (those past the column masked
+            // off), whatever the column's size
+            for (int w0 = threadIdx.x; w0 < col_words; w0 += U * kPieceThreads) {
+                v4u v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int w = w0 + u * kPieceThreads;
+                    v[u] = w < col_words ? __builtin_nontemporal_load(base + piece_word(w, s, row_words, piece_words))
+                                         : v4u{0u, 0u, 0u, 0u};
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+            }
+        }
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;   // almost never true; keeps every load live
+}
+
+template <bool NT>
+__global__ __launch_bounds__(kPieceThreads) void probe_write_pieces_kernel(
+    v4u* __restrict__ dst, size_t panels, int rows, int row_words, int piece_words, uint32_t pattern) {
+    const int col_words = rows * piece_words;
+    const v4u v = {pattern, pattern + 1u, pattern + 2u, pattern + 3u};
+    for (size_t p = blockIdx.x; p < panels; p += gridDim.x) {
+        v4u* base = dst + p * static_cast<size_t>(rows) * row_words;
+        for (int s = 0; s < row_words; s += piece_words)
+            for (int w0 = threadIdx.x; w0 < col_words; w0 += 8 * kPieceThreads) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int w = w0 + u * kPieceThreads;
+                    if (w >= col_words) break;
+                    v4u* q = base + piece_word(w, s, row_words, piece_words);
+                    if (NT) __builtin_nontemporal_store(v, q); else *q = v;
+                }
+            }
+    }
+}
+
+// ---- LDS-DMA ring probe: the GEMMs' load pipeline without their compute.
+// One 512-thread workgroup per CU streams contiguous 1 MiB panels in 32 KiB
+// slabs through NS LDS stages: each wave issues its 1 KiB DMA blocks of the
+// slab NS-1 ahead, waits until its loads of the current slab have landed,
+// and the workgroup meets at a barrier, once per slab.
+constexpr int kRingSlab = 32 * 1024, kRingPanel = 1 << 20;
+
+template <int NS>
+__global__ __launch_bounds__(kPieceThreads) void probe_lds_ring_kernel(const uint8_t* __restrict__ src,
+                                                                        size_t panels,
+                                                                        uint32_t* __restrict__ sink) {
+    constexpr int NW = kPieceThreads / kWave, INST = kRingSlab / 1024 / NW, SLABS = kRingPanel / kRingSlab;
+    static_assert(NS >= 2 && NS <= 5 && INST >= 1, "ring");
+    __shared__ __attribute__((aligned(1024))) uint8_t smem[NS * kRingSlab];
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+    const int lane = threadIdx.x & (kWave - 1);
+    const uint32_t lds0 = lds_addr(smem);
+    uint32_t acc = 0;
+    for (size_t p = blockIdx.x; p < panels; p += gridDim.x) {
+        const i32x4 r = make_rsrc(src + p * kRingPanel, kRingPanel);
+        auto issue = [&](int slab) {   // slabs past the panel read zeros (uniform wait counts)
+#pragma unroll
+            for (int i = 0; i < INST; ++i) {
+                const uint32_t blk = static_cast<uint32_t>(wave + i * NW) * 1024u;
+                const uint32_t off = slab < SLABS ? static_cast<uint32_t>(slab) * kRingSlab + blk + lane * 16u : kOob;
+                dma16<true>(r, off, lds0 + (slab % NS) * kRingSlab + blk);
+            }
+        };
+#pragma unroll
+        for (int s = 0; s < NS - 1; ++s) issue(s);
+        for (int s = 0; s < SLABS; ++s) {
+            // slab s has landed once at most the NS-2 later slabs' loads are pending
+            if constexpr (NS == 2) wait_vmcnt<0>();
+            else if constexpr (NS == 3) wait_vmcnt<INST>();
+            else if constexpr (NS == 4) wait_vmcnt<2 * INST>();
+            else wait_vmcnt<3 * INST>();
+            __syncthreads();
+            issue(s + NS - 1);
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+        acc ^= reinterpret_cast<const uint32_t*>(smem)[threadIdx.x];
+        __syncthreads();                  // the next panel's loads refill the stages
+    }
+    if (acc == 0x9E3779B9u) sink[0] = acc;
+}
+
 int probe_grid() {
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -124,5 +232,82 @@ extern "C" int moe_probe_copy(const void* src, void* dst, size_t bytes, hipStrea
     if (bytes == 0) return MOE_OK;
     probe_copy_kernel<<<probe_grid(), kProbeThreads, 0, stream>>>(static_cast<const v4u*>(src),
                                                                   static_cast<v4u*>(dst), bytes / 16);
+    return launch_status();
+}
+
+namespace moe {
+namespace {
+
+int device_cu_count() {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        cus = 1;
+    return cus;
+}
+
+// panels of `rows` rows of row_bytes, visited in pieces of piece_bytes
+int check_pieces(const void* p, size_t bytes, int32_t row_bytes, int32_t rows, int32_t piece_bytes,
+                 size_t* panels) {
+    int st = check_probe(p, bytes);
+    if (st != MOE_OK) return st;
+    if (row_bytes < 16 || rows < 1 || piece_bytes < 16) return MOE_ERR_INVALID_ARG;
+    if (row_bytes % 16 || piece_bytes % 16 || row_bytes % piece_bytes) return MOE_ERR_MISALIGNED;
+    const int64_t panel = static_cast<int64_t>(rows) * row_bytes;
+    if (panel / 16 > INT32_MAX) return MOE_ERR_UNSUPPORTED;
+    if (bytes % static_cast<size_t>(panel)) return MOE_ERR_INVALID_ARG;
+    *panels = bytes / static_cast<size_t>(panel);
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_probe_read_pieces(const void* src, size_t bytes, int32_t row_bytes, int32_t rows,
+                                     int32_t piece_bytes, uint32_t* sink, hipStream_t stream) {
+    using namespace moe;
+    size_t panels = 0;
+    int st = check_pieces(src, bytes, row_bytes, rows, piece_bytes, &panels);
+    if (st != MOE_OK) return st;
+    if (!sink) return MOE_ERR_INVALID_ARG;
+    if (bytes == 0) return MOE_OK;
+    probe_read_pieces_kernel<<<device_cu_count(), kPieceThreads, 0, stream>>>(
+        static_cast<const v4u*>(src), panels, rows, row_bytes / 16, piece_bytes / 16, sink);
+    return launch_status();
+}
+
+extern "C" int moe_probe_write_pieces(void* dst, size_t bytes, int32_t row_bytes, int32_t rows,
+                                      int32_t piece_bytes, int32_t nontemporal, hipStream_t stream) {
+    using namespace moe;
+    size_t panels = 0;
+    int st = check_pieces(dst, bytes, row_bytes, rows, piece_bytes, &panels);
+    if (st != MOE_OK) return st;
+    if (bytes == 0) return MOE_OK;
+    if (nontemporal)
+        probe_write_pieces_kernel<true><<<device_cu_count(), kPieceThreads, 0, stream>>>(
+            static_cast<v4u*>(dst), panels, rows, row_bytes / 16, piece_bytes / 16, 0x3C3C0000u);
+    else
+        probe_write_pieces_kernel<false><<<device_cu_count(), kPieceThreads, 0, stream>>>(
+            static_cast<v4u*>(dst), panels, rows, row_bytes / 16, piece_bytes / 16, 0x3C3C0000u);
+    return launch_status();
+}
+
+extern "C" int moe_probe_lds_ring(const void* src, size_t bytes, int32_t stages, uint32_t* sink,
+                                  hipStream_t stream) {
+    using namespace moe;
+    int st = check_probe(src, bytes);
+    if (st != MOE_OK) return st;
+    if (!sink) return MOE_ERR_INVALID_ARG;
+    if (stages < 2 || stages > 5 || bytes % kRingPanel) return MOE_ERR_INVALID_ARG;
+    if (bytes == 0) return MOE_OK;
+    const size_t panels = bytes / kRingPanel;
+    const int g = device_cu_count();
+    const uint8_t* s8 = static_cast<const uint8_t*>(src);
+    switch (stages) {
+        case 2: probe_lds_ring_kernel<2><<<g, kPieceThreads, 0, stream>>>(s8, panels, sink); break;
+        case 3: probe_lds_ring_kernel<3><<<g, kPieceThreads, 0, stream>>>(s8, panels, sink); break;
+        case 4: probe_lds_ring_kernel<4><<<g, kPieceThreads, 0, stream>>>(s8, panels, sink); break;
+        default: probe_lds_ring_kernel<5><<<g, kPieceThreads, 0, stream>>>(s8, panels, sink); break;
+    }
     return launch_status();
 }

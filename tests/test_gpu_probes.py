@@ -1,7 +1,8 @@
 """The HBM rate probes do what their rates assume: the copy reproduces its
 source byte for byte and the write fills every 16-byte word of its buffer,
-for sizes that leave partial chunks (the read is checked only for running
-through the buffer)."""
+for sizes that leave partial chunks; the access-order write fills every word
+in each piece order and policy (the reads, and the LDS ring, are checked for
+running through the buffer)."""
 
 import pytest
 import torch
@@ -26,4 +27,28 @@ def test_probe_copy_write_read(nbytes):
     assert torch.equal(words, expect.expand_as(words))
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     moe.moe_probe_read(src, sink)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("piece,nt", [(128, True), (512, False), (4096, True), (48, False)])
+def test_access_order_write_covers_every_word(piece, nt):
+    row_bytes = 4096 if piece != 48 else 96 * 16
+    rows, panels = 256, 3
+    dst = torch.zeros(panels * rows * row_bytes, dtype=torch.uint8, device="cuda")
+    moe.moe_probe_write_pieces(dst, row_bytes, rows, piece, nt)
+    torch.cuda.synchronize()
+    words = dst.view(torch.int32).view(-1, 4)
+    expect = torch.tensor([0x3C3C0000, 0x3C3C0001, 0x3C3C0002, 0x3C3C0003], dtype=torch.int32,
+                          device="cuda")
+    assert torch.equal(words, expect.expand_as(words))
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    moe.moe_probe_read_pieces(dst, row_bytes, rows, piece, sink)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("stages", [2, 3, 4, 5])
+def test_lds_ring_runs(stages):
+    src = torch.randint(0, 256, (3 << 20,), dtype=torch.uint8, device="cuda")
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    moe.moe_probe_lds_ring(src, stages, sink)
     torch.cuda.synchronize()

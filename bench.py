@@ -229,7 +229,9 @@ def access_order_probes(torch, moe, w, reps=10):
     """GB/s of the library's access-order probes over a buffer the size of
     the workload's W1 ([E, 2I, H] bf16, as panels of 256 rows of H*2 bytes):
     reads and writes in the order a GEMM tile walks a weight panel (pieces of
-    128, 256 or 512 bytes of every row in turn) against front to back, and the
+    128, 256 or 512 bytes of every row in turn) against front to back, writes
+    in the order the weight-gradient GEMM's output tiles reach memory (tiles
+    of 256 rows x 512 or 1024 bytes, neighbouring tiles on one XCD), and the
     GEMMs' LDS-DMA ring alone at 2-5 stages.  Prints one JSON line."""
     row = w.H * 2
     panel = 256 * row
@@ -254,7 +256,8 @@ def access_order_probes(torch, moe, w, reps=10):
 
     out = {"probe": "access_order", "workload": w.name, "buffer_bytes": nbytes, "row_bytes": row,
            "rows_per_panel": 256, "reps": reps,
-           "read_gbs": {}, "write_gbs": {"nontemporal": {}, "default": {}}, "lds_ring_gbs": {}}
+           "read_gbs": {}, "write_gbs": {"nontemporal": {}, "default": {}},
+           "write_tiles_gbs": {"nontemporal": {}, "default": {}}, "lds_ring_gbs": {}}
     moe.moe_probe_write(buf, stream)
     for p in pieces:
         key = "front_to_back" if p == row else str(p)
@@ -262,9 +265,16 @@ def access_order_probes(torch, moe, w, reps=10):
         for nt in (True, False):
             out["write_gbs"]["nontemporal" if nt else "default"][key] = rate(
                 lambda: moe.moe_probe_write_pieces(buf, row, 256, p, nt, stream))
+    for p in (512, 1024):
+        if row % p:
+            continue
+        for nt in (True, False):
+            out["write_tiles_gbs"]["nontemporal" if nt else "default"][str(p)] = rate(
+                lambda: moe.moe_probe_write_tiles(buf, row, 256, p, nt, stream))
     for st in (2, 3, 4, 5):
         out["lds_ring_gbs"][str(st)] = rate(lambda: moe.moe_probe_lds_ring(buf, st, sink, stream))
-    log("[bench] access-order probes GB/s: " + json.dumps({k: out[k] for k in ("read_gbs", "write_gbs", "lds_ring_gbs")}))
+    log("[bench] access-order probes GB/s: " + json.dumps(
+        {k: out[k] for k in ("read_gbs", "write_gbs", "write_tiles_gbs", "lds_ring_gbs")}))
     print(json.dumps(out))
 
 

@@ -53,11 +53,19 @@ int moe_probe_copy(const void* src, void* dst, size_t bytes, hipStream_t stream)
  * moe_probe_read_pieces reads every byte once (non-temporal loads) and
  * writes at most one word to sink[0] (its value means nothing);
  * moe_probe_write_pieces writes every byte once with a fixed pattern,
- * non-temporal stores when `nontemporal` is nonzero. */
+ * non-temporal stores when `nontemporal` is nonzero.
+ *
+ * moe_probe_write_tiles writes the same bytes (same pattern, same argument
+ * rules) in the order the weight-gradient GEMM's output tiles reach memory:
+ * each piece column of a panel (rows x piece_bytes) is a tile written whole,
+ * row after row, by one workgroup, and the pieces of one panel go to
+ * neighbouring workgroups of one XCD, so they are written at the same time. */
 int moe_probe_read_pieces(const void* src, size_t bytes, int32_t row_bytes, int32_t rows,
                           int32_t piece_bytes, uint32_t* sink, hipStream_t stream);
 int moe_probe_write_pieces(void* dst, size_t bytes, int32_t row_bytes, int32_t rows,
                            int32_t piece_bytes, int32_t nontemporal, hipStream_t stream);
+int moe_probe_write_tiles(void* dst, size_t bytes, int32_t row_bytes, int32_t rows,
+                          int32_t piece_bytes, int32_t nontemporal, hipStream_t stream);
 
 /* The GEMMs' load pipeline without their compute: one 512-thread workgroup
  * per compute unit streams contiguous 1 MiB panels of src in 32 KiB slabs

@@ -35,6 +35,7 @@ from ._native import (  # noqa: F401
     moe_probe_read_pieces,
     moe_probe_write,
     moe_probe_write_pieces,
+    moe_probe_write_tiles,
     PROBE_HEADER_PATH,
     moe_route_bwd,
     moe_route_capacity,

@@ -80,6 +80,7 @@ _SIGNATURES = {
     "moe_probe_copy": (ctypes.c_int, [_vp, _vp, ctypes.c_size_t, _vp]),
     "moe_probe_read_pieces": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _i32, _vp, _vp]),
     "moe_probe_write_pieces": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _i32, _i32, _vp]),
+    "moe_probe_write_tiles": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _i32, _i32, _vp]),
     "moe_probe_lds_ring": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
@@ -136,6 +137,15 @@ def moe_probe_write_pieces(dst, row_bytes: int, rows: int, piece_bytes: int, non
     (an access-order probe)."""
     p, n = _bytes_ptr(dst, "dst")
     _check("moe_probe_write_pieces", lib.moe_probe_write_pieces(
+        p, n, row_bytes, rows, piece_bytes, int(bool(nontemporal)), _stream(stream)))
+
+
+def moe_probe_write_tiles(dst, row_bytes: int, rows: int, piece_bytes: int, nontemporal: bool,
+                          stream=None):
+    """Write dst as panels of rows x row_bytes in tiles of rows x piece_bytes,
+    neighbouring tiles on one XCD (an access-order probe)."""
+    p, n = _bytes_ptr(dst, "dst")
+    _check("moe_probe_write_tiles", lib.moe_probe_write_tiles(
         p, n, row_bytes, rows, piece_bytes, int(bool(nontemporal)), _stream(stream)))
 
 

@@ -141,6 +141,35 @@ __global__ __launch_bounds__(kPieceThreads) void probe_write_pieces_kernel(
     }
 }
 
+// The same panels cut into tiles of rows x piece_words (tile t = panel *
+// pieces + piece, the piece fastest), each written whole by one workgroup,
+// row after row; workgroup w writes tiles r(w), r(w) + G, ... with r the
+// GEMMs' XCD renumbering, so the pieces of one panel are written at once by
+// neighbouring workgroups of one XCD -- the order in which the
+// weight-gradient GEMM's 256-column output tiles reach memory.
+template <bool NT>
+__global__ __launch_bounds__(kPieceThreads) void probe_write_tiles_kernel(
+    v4u* __restrict__ dst, size_t panels, int rows, int row_words, int piece_words, uint32_t pattern) {
+    const int pieces = row_words / piece_words;
+    const int tile_words = rows * piece_words;
+    const size_t tiles = panels * static_cast<size_t>(pieces);
+    const v4u v = {pattern, pattern + 1u, pattern + 2u, pattern + 3u};
+    for (size_t t = xcd_remap(blockIdx.x, gridDim.x); t < tiles; t += gridDim.x) {
+        const size_t p = t / pieces;
+        const int s = static_cast<int>(t - p * pieces) * piece_words;
+        v4u* base = dst + p * static_cast<size_t>(rows) * row_words;
+        for (int w0 = threadIdx.x; w0 < tile_words; w0 += 8 * kPieceThreads) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int w = w0 + u * kPieceThreads;
+                if (w >= tile_words) break;
+                v4u* q = base + piece_word(w, s, row_words, piece_words);
+                if (NT) __builtin_nontemporal_store(v, q); else *q = v;
+            }
+        }
+    }
+}
+
 // ---- LDS-DMA ring probe: the GEMMs' load pipeline without their compute.
 // One 512-thread workgroup per CU streams contiguous 1 MiB panels in 32 KiB
 // slabs through NS LDS stages: each wave issues its 1 KiB DMA blocks of the
@@ -288,6 +317,22 @@ extern "C" int moe_probe_write_pieces(void* dst, size_t bytes, int32_t row_bytes
             static_cast<v4u*>(dst), panels, rows, row_bytes / 16, piece_bytes / 16, 0x3C3C0000u);
     else
         probe_write_pieces_kernel<false><<<device_cu_count(), kPieceThreads, 0, stream>>>(
+            static_cast<v4u*>(dst), panels, rows, row_bytes / 16, piece_bytes / 16, 0x3C3C0000u);
+    return launch_status();
+}
+
+extern "C" int moe_probe_write_tiles(void* dst, size_t bytes, int32_t row_bytes, int32_t rows,
+                                     int32_t piece_bytes, int32_t nontemporal, hipStream_t stream) {
+    using namespace moe;
+    size_t panels = 0;
+    int st = check_pieces(dst, bytes, row_bytes, rows, piece_bytes, &panels);
+    if (st != MOE_OK) return st;
+    if (bytes == 0) return MOE_OK;
+    if (nontemporal)
+        probe_write_tiles_kernel<true><<<device_cu_count(), kPieceThreads, 0, stream>>>(
+            static_cast<v4u*>(dst), panels, rows, row_bytes / 16, piece_bytes / 16, 0x3C3C0000u);
+    else
+        probe_write_tiles_kernel<false><<<device_cu_count(), kPieceThreads, 0, stream>>>(
             static_cast<v4u*>(dst), panels, rows, row_bytes / 16, piece_bytes / 16, 0x3C3C0000u);
     return launch_status();
 }

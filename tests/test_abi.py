@@ -36,7 +36,8 @@ def test_every_declared_symbol_is_exported():
 def test_probe_header_symbols_and_validation():
     names = moe.header_functions(moe.PROBE_HEADER_PATH)
     assert set(names) == {"moe_probe_read", "moe_probe_write", "moe_probe_copy",
-                          "moe_probe_read_pieces", "moe_probe_write_pieces", "moe_probe_lds_ring"}
+                          "moe_probe_read_pieces", "moe_probe_write_pieces", "moe_probe_write_tiles",
+                          "moe_probe_lds_ring"}
     for n in names:
         assert hasattr(lib, n), n
     big = ctypes.c_size_t(1 << 20)
@@ -60,6 +61,13 @@ def test_probe_header_symbols_and_validation():
     assert lib.moe_probe_read_pieces(ALIGNED, ctypes.c_size_t(0), 4096, 256, 128, ALIGNED, NUL) == OK
     assert lib.moe_probe_write_pieces(ALIGNED, panel, 4008, 256, 16, 0, NUL) == MISALIGNED
     assert lib.moe_probe_write_pieces(ALIGNED, ctypes.c_size_t(0), 4096, 256, 512, 1, NUL) == OK
+    assert lib.moe_probe_write_tiles(NUL, panel, 4096, 256, 512, 1, NUL) == INVALID
+    assert lib.moe_probe_write_tiles(MIS, panel, 4096, 256, 512, 1, NUL) == MISALIGNED
+    assert lib.moe_probe_write_tiles(ALIGNED, panel, 4096, 256, 96, 1, NUL) == MISALIGNED
+    assert lib.moe_probe_write_tiles(ALIGNED, panel, 4096, 0, 512, 0, NUL) == INVALID
+    assert lib.moe_probe_write_tiles(ALIGNED, ctypes.c_size_t(4096 * 100), 4096, 256, 512, 0,
+                                     NUL) == INVALID                      # not whole panels
+    assert lib.moe_probe_write_tiles(ALIGNED, ctypes.c_size_t(0), 4096, 256, 512, 0, NUL) == OK
     assert lib.moe_probe_lds_ring(ALIGNED, big, 1, ALIGNED, NUL) == INVALID
     assert lib.moe_probe_lds_ring(ALIGNED, big, 6, ALIGNED, NUL) == INVALID
     assert lib.moe_probe_lds_ring(ALIGNED, ctypes.c_size_t(4096), 3, ALIGNED, NUL) == INVALID

@@ -1,8 +1,9 @@
 """The HBM rate probes do what their rates assume: the copy reproduces its
 source byte for byte and the write fills every 16-byte word of its buffer,
-for sizes that leave partial chunks; the access-order write fills every word
-in each piece order and policy (the reads, and the LDS ring, are checked for
-running through the buffer)."""
+for sizes that leave partial chunks; the access-order writes (piece columns
+per workgroup, and tiles dealt over the XCDs) fill every word in each piece
+order and policy (the reads, and the LDS ring, are checked for running
+through the buffer)."""
 
 import pytest
 import torch
@@ -44,6 +45,19 @@ def test_access_order_write_covers_every_word(piece, nt):
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     moe.moe_probe_read_pieces(dst, row_bytes, rows, piece, sink)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("piece,nt,panels", [(512, True, 3), (1024, False, 5), (4096, True, 2), (48, False, 7)])
+def test_tile_order_write_covers_every_word(piece, nt, panels):
+    row_bytes = 4096 if piece != 48 else 96 * 16
+    rows = 256
+    dst = torch.zeros(panels * rows * row_bytes, dtype=torch.uint8, device="cuda")
+    moe.moe_probe_write_tiles(dst, row_bytes, rows, piece, nt)
+    torch.cuda.synchronize()
+    words = dst.view(torch.int32).view(-1, 4)
+    expect = torch.tensor([0x3C3C0000, 0x3C3C0001, 0x3C3C0002, 0x3C3C0003], dtype=torch.int32,
+                          device="cuda")
+    assert torch.equal(words, expect.expand_as(words))
 
 
 @pytest.mark.parametrize("stages", [2, 3, 4, 5])

@@ -49,9 +49,12 @@ from .backward import (  # noqa: F401
     fc1_preact,
     fc1_preact_slots,
     fc1_wgrad,
+    fc1_wgrad_sum,
     fc2_dgrad,
     fc2_wgrad,
+    fc2_wgrad_sum,
     grouped_ffn_backward,
+    main_grad_accumulate,
     route_backward,
     swiglu_backward,
 )

@@ -26,6 +26,9 @@ expert_backward       one expert: FC2 dgrad, SwiGLU bwd, FC1 dgrad,     finite d
 grouped_ffn_backward  every expert over the route list                  as above
 route_backward        softmax-over-top-K gradient of the router logits  finite differences,
                                                                         zero row sums, K = 1
+main_grad_accumulate  a float32 main gradient plus a weight gradient    linearity over
+                      (section 5: the weight-gradient GEMM can add      micro-batches
+                      into a float32 main gradient inside the kernel)
 backward              the whole layer: dx, dW1, dW2, d_logits           finite differences,
                                                                         autograd (exact mode)
 ====================  ================================================  =====================
@@ -219,22 +222,40 @@ def fc1_dgrad(d_preact, w1, E: int, Cp: int):
     return f64_to_bf16_bits(out)
 
 
-def fc2_wgrad(dy, act, sorted_slot_ids, E: int, Cp: int):
-    """dW2[e] = bf16(sum over e's slots of dy[row(s)]^T act[s]) (bf16 bits)."""
+def fc2_wgrad_sum(dy, act, sorted_slot_ids, E: int, Cp: int):
+    """sum over e's slots of dy[row(s)]^T act[s], float64 [E, H, I], unrounded."""
     dyf = _f64(dy)
     af = _f64(act)
-    out = np.stack([_gather_rows(dyf, sorted_slot_ids, e * Cp, (e + 1) * Cp).T @ af[e * Cp:(e + 1) * Cp]
-                    for e in range(E)])
-    return f64_to_bf16_bits(out)
+    return np.stack([_gather_rows(dyf, sorted_slot_ids, e * Cp, (e + 1) * Cp).T @ af[e * Cp:(e + 1) * Cp]
+                     for e in range(E)])
+
+
+def fc2_wgrad(dy, act, sorted_slot_ids, E: int, Cp: int):
+    """dW2[e] = bf16(sum over e's slots of dy[row(s)]^T act[s]) (bf16 bits)."""
+    return f64_to_bf16_bits(fc2_wgrad_sum(dy, act, sorted_slot_ids, E, Cp))
+
+
+def fc1_wgrad_sum(d_preact, x, sorted_slot_ids, E: int, Cp: int):
+    """sum over e's slots of d_preact[s]^T x[row(s)], float64 [E, 2I, H], unrounded."""
+    dp = _f64(d_preact)
+    xf = _f64(x)
+    return np.stack([dp[e * Cp:(e + 1) * Cp].T @ _gather_rows(xf, sorted_slot_ids, e * Cp, (e + 1) * Cp)
+                     for e in range(E)])
 
 
 def fc1_wgrad(d_preact, x, sorted_slot_ids, E: int, Cp: int):
     """dW1[e] = bf16(sum over e's slots of d_preact[s]^T x[row(s)]) (bf16 bits)."""
-    dp = _f64(d_preact)
-    xf = _f64(x)
-    out = np.stack([dp[e * Cp:(e + 1) * Cp].T @ _gather_rows(xf, sorted_slot_ids, e * Cp, (e + 1) * Cp)
-                    for e in range(E)])
-    return f64_to_bf16_bits(out)
+    return f64_to_bf16_bits(fc1_wgrad_sum(d_preact, x, sorted_slot_ids, E, Cp))
+
+
+def main_grad_accumulate(main, dw_sum):
+    """A float32 main gradient after a weight gradient is added into it
+    ([PF] section 5: the weight-gradient GEMM writes bf16 or accumulates into
+    a float32 main gradient): main + dW, in float64 (main: float32 values,
+    dw_sum: the unrounded sums of fc1_wgrad_sum / fc2_wgrad_sum).  Over
+    micro-batches this is gradient accumulation: the sum of the batches'
+    weight gradients."""
+    return np.asarray(main, dtype=np.float64) + np.asarray(dw_sum, dtype=np.float64)
 
 
 def fc1_preact_slots(x, w1, sorted_slot_ids, E: int, Cp: int):

@@ -221,3 +221,44 @@ def test_stepwise_functions_chain_to_grouped_backward():
     assert np.array_equal(oracle.fc1_dgrad(d_pre, w1, E, Cp), G["d_a"])
     assert np.array_equal(oracle.fc2_wgrad(dy, act, ssi, E, Cp), G["dw2"])
     assert np.array_equal(oracle.fc1_wgrad(d_pre, x, ssi, E, Cp), G["dw1"])
+
+
+def test_main_grad_accumulation_is_linear_over_micro_batches():
+    """Accumulating two micro-batches' weight gradients into a zero main
+    gradient gives the weight gradient of both batches' slots contracted at
+    once (each expert's segments of the two batches stacked into one
+    contraction of 2*Cp slots); a non-zero starting main gradient is carried
+    through unchanged."""
+    rng = np.random.default_rng(7)
+    N, H, I, E, Cp = 20, 8, 6, 3, 4
+
+    def bf(a):
+        return moe_inputs.bf16_bits(torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16))
+
+    x = [bf(rng.standard_normal((N, H))) for _ in range(2)]
+    dy = [bf(rng.standard_normal((N, H))) for _ in range(2)]
+    dpre = [bf(rng.standard_normal((E * Cp, 2 * I))) for _ in range(2)]
+    act = [bf(rng.standard_normal((E * Cp, I))) for _ in range(2)]
+    ssi = [rng.integers(0, N + 1, E * Cp).astype(np.int32) for _ in range(2)]   # N: pad slot
+    main1 = rng.standard_normal((E, 2 * I, H)).astype(np.float32)
+    main2 = rng.standard_normal((E, H, I)).astype(np.float32)
+    acc1 = oracle.main_grad_accumulate(np.zeros_like(main1), oracle.fc1_wgrad_sum(dpre[0], x[0], ssi[0], E, Cp))
+    acc1 = oracle.main_grad_accumulate(acc1, oracle.fc1_wgrad_sum(dpre[1], x[1], ssi[1], E, Cp))
+    acc2 = oracle.main_grad_accumulate(main2, oracle.fc2_wgrad_sum(dy[0], act[0], ssi[0], E, Cp))
+    acc2 = oracle.main_grad_accumulate(acc2, oracle.fc2_wgrad_sum(dy[1], act[1], ssi[1], E, Cp))
+    # both batches as one contraction: token rows of batch b offset by b*N
+    # (pads keep pointing at a zero row, index 2N)
+    xs, dys = np.concatenate(x), np.concatenate(dy)
+
+    def stack(a):
+        return np.concatenate([np.concatenate([a[0][e * Cp:(e + 1) * Cp], a[1][e * Cp:(e + 1) * Cp]])
+                               for e in range(E)])
+
+    ss = [np.where(ssi[b] == N, 2 * N, ssi[b] + b * N) for b in range(2)]
+    both1 = oracle.fc1_wgrad_sum(stack(dpre), xs, stack(ss), E, 2 * Cp)
+    both2 = oracle.fc2_wgrad_sum(dys, stack(act), stack(ss), E, 2 * Cp)
+    np.testing.assert_allclose(acc1, both1, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(acc2, main2.astype(np.float64) + both2, rtol=1e-12, atol=1e-12)
+    # and the bf16 forms are these sums rounded
+    assert np.array_equal(oracle.fc1_wgrad(dpre[0], x[0], ssi[0], E, Cp),
+                          oracle.f64_to_bf16_bits(oracle.fc1_wgrad_sum(dpre[0], x[0], ssi[0], E, Cp)))

@@ -23,7 +23,8 @@ block-padded segments, the extent a device scalar): its own JSON line, with
 the algorithmic work taken at the real padded extent.  --variant backward
 measures the layer's training step (forward keeping the pre-activation, then
 the backward for a seeded dy), with the roofline of the slowest backward
-kernel.  --variant serving measures variable-N serving of the dropless form
+kernel; with --main-grad the weight gradients are added into float32 main
+gradients instead of written as bf16.  --variant serving measures variable-N serving of the dropless form
 from a ladder of captured bucket graphs against one graph at the worst-case
 shape and against eager launches (a seeded stream of item sizes).
 --variant ep-local measures the grouped FFN on one expert-parallel rank's
@@ -437,11 +438,14 @@ def roofline(name, flops, nbytes, us, traffic=None, probes=None):
             "frac": tflops / PEAK_BF16_TFLOPS, "hbm_gbs": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, **common}
 
 
-def backward_work(w, Cp, kept):
+def backward_work(w, Cp, kept, main_grad=False):
     """Algorithmic work of each call of the training step (forward keeping
-    the pre-activation, then the backward): (flops, bytes) per call."""
+    the pre-activation, then the backward): (flops, bytes) per call.
+    main_grad: the weight gradients are added into float32 main gradients
+    (each read and written once, 8 bytes per element instead of 2)."""
     N, H, I, E, K = w.N, w.H, w.I, w.E, w.K
     R = E * Cp
+    dwb = 8 if main_grad else 2
     route = N * E * 4 + N * K * (4 + 4) * 2 + N * K * 4 + E * 4 \
         + R * 8 + (R // 32) * 4 + E * 4 + N * K * 4 + N * 4 + 4
     return {
@@ -457,8 +461,8 @@ def backward_work(w, Cp, kept):
         "fc1_dgrad": (2.0 * R * 2 * I * H, E * 2 * I * H * 2 + R * 2 * I * 2 + R * H * 2),
         "dx_combine": (0.0, kept * H * 2 + N * K * 4 + N * H * 2),
         # dy rows once, act in, dW2 out
-        "fc2_wgrad": (2.0 * R * H * I, N * H * 2 + R * 4 + R * I * 2 + E * H * I * 2),
-        "fc1_wgrad": (2.0 * R * 2 * I * H, R * 2 * I * 2 + N * H * 2 + R * 4 + E * 2 * I * H * 2),
+        "fc2_wgrad": (2.0 * R * H * I, N * H * 2 + R * 4 + R * I * 2 + E * H * I * dwb),
+        "fc1_wgrad": (2.0 * R * 2 * I * H, R * 2 * I * 2 + N * H * 2 + R * 4 + E * 2 * I * H * dwb),
         "route_bwd": (0.0, N * K * (4 + 4 + 4 + 4) + N * E * 4),
     }
 
@@ -468,7 +472,7 @@ def bench_backward(args, w, T, torch, moe):
     pre-activation, FC2, combine, then the whole backward for a seeded dy."""
     import moe_inputs
     buf = moe.MoEBuffers(w.N, w.H, w.I, w.E, w.K, w.F, "cuda")
-    bw = moe.MoEBackwardBuffers(buf)
+    bw = moe.MoEBackwardBuffers(buf, main_grad=args.main_grad)
     dy = moe_inputs.make_dy(w, "cuda")
     x, w1, w2 = T["x"], T["w1"], T["w2"]
     names = ["route_capacity_align", "fc1_save", "fc2", "combine", "fc2_dgrad", "swiglu_bwd",
@@ -487,7 +491,7 @@ def bench_backward(args, w, T, torch, moe):
     ms_per_step = time_graph(torch, step, stream, args)
     us = time_calls(torch, names, calls, stream, args)
     kept = int((buf.token_routes >= 0).sum().item())
-    work = backward_work(w, buf.Cp, kept)
+    work = backward_work(w, buf.Cp, kept, args.main_grad)
     bwd_names = names[4:]
     dom = max(bwd_names, key=lambda n: us[n])
     gemms = ["fc1_save", "fc2", "fc2_dgrad", "fc1_dgrad", "fc2_wgrad", "fc1_wgrad"]
@@ -507,8 +511,11 @@ def bench_backward(args, w, T, torch, moe):
         "dtype": "bf16",
         "data": "synthetic",
         "env": provenance(torch),
-        "config": {"workload": w.name + "/fwd+bwd", "N": w.N, "H": w.H, "E": w.E, "K": w.K,
+        "config": {"workload": w.name + ("/fwd+bwd+main_grad" if args.main_grad else "/fwd+bwd"),
+                   "N": w.N, "H": w.H, "E": w.E, "K": w.K,
                    "I": w.I, "F": w.F, "C": buf.C, "Cp": buf.Cp,
+                   "weight_gradients": ("added into float32 main gradients" if args.main_grad
+                                        else "written as bf16"),
                    "timed": "hipGraph replay of forward (pre-activation kept) + backward"},
         "gemm_tflops": gflops / (gus * 1e-6) / 1e12,
         "gemm_frac_bf16_peak": gflops / (gus * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
@@ -785,6 +792,9 @@ def main():
                     default="capacity",
                     help="fixed-capacity forward (the headline), the dropless form, or the "
                          "training step (forward keeping the pre-activation + backward)")
+    ap.add_argument("--main-grad", action="store_true",
+                    help="with --variant backward: add the weight gradients into float32 main "
+                         "gradients (gradient accumulation) instead of writing them as bf16")
     ap.add_argument("--vendor-reference", action="store_true",
                     help="only time torch's bf16 batched GEMM (hipBLASLt) at the layer's per-expert "
                          "FC1 and FC2 shapes, as context for the grouped kernels, and exit")

@@ -432,6 +432,27 @@ int moe_grouped_fc1_wgrad(const uint16_t* d_preact, const uint16_t* x,
                           const int32_t* sorted_slot_ids, int64_t N, int32_t H, int32_t I,
                           int32_t E, int64_t C, uint16_t* dw1, hipStream_t stream);
 
+/* Weight gradients added into float32 main gradients, for gradient
+ * accumulation over micro-batches ([PF] section 5: the weight-gradient GEMM
+ * writes bf16 or accumulates into a float32 main gradient inside the kernel):
+ *   moe_grouped_fc2_wgrad_accum  main_dw2[e] += sum_s dy[row(s)]^T act[s]
+ *   moe_grouped_fc1_wgrad_accum  main_dw1[e] += sum_s d_preact[s]^T x[row(s)]
+ * with the same inputs as moe_grouped_fc2_wgrad / moe_grouped_fc1_wgrad;
+ * main_dw2 in/out float32 [E, H, I], main_dw1 in/out float32 [E, 2I, H],
+ * 16-byte aligned, owned by the caller.  Each element becomes
+ * float32(old + sum), sum being the float32 accumulation the bf16 entry
+ * points round (so rounding the result of an accumulation into zeros gives
+ * their output bit for bit); every element has one writer, no atomics, so
+ * the result does not depend on the schedule.  N == 0 or C == 0 leaves
+ * main_dw as it is (the sums are zero).  MOE_ERR_UNSUPPORTED also when one
+ * expert's float32 gradient (2*I*H*4 bytes) reaches 2 GiB. */
+int moe_grouped_fc2_wgrad_accum(const uint16_t* dy, const uint16_t* act,
+                                const int32_t* sorted_slot_ids, int64_t N, int32_t H, int32_t I,
+                                int32_t E, int64_t C, float* main_dw2, hipStream_t stream);
+int moe_grouped_fc1_wgrad_accum(const uint16_t* d_preact, const uint16_t* x,
+                                const int32_t* sorted_slot_ids, int64_t N, int32_t H, int32_t I,
+                                int32_t E, int64_t C, float* main_dw1, hipStream_t stream);
+
 /* Router-logit gradient through the softmax over each token's top K.  Route
  * (t, k) takes dp = d_prob[token_routes[t, k]] (0 if dropped, or if the index
  * is outside [0, R)); with p = topk_probs[t]:

@@ -20,11 +20,13 @@ from ._native import (  # noqa: F401
     moe_grouped_fc1_swiglu_dropless,
     moe_grouped_fc1_swiglu_save,
     moe_grouped_fc1_wgrad,
+    moe_grouped_fc1_wgrad_accum,
     moe_grouped_fc2,
     moe_grouped_fc2_rows,
     moe_grouped_fc2_dgrad,
     moe_grouped_fc2_dropless,
     moe_grouped_fc2_wgrad,
+    moe_grouped_fc2_wgrad_accum,
     moe_grouped_ffn_fwd,
     moe_grouped_ffn_fwd_dropless,
     moe_layout_block_m,

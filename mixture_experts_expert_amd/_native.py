@@ -74,6 +74,10 @@ _SIGNATURES = {
                                              _vp]),
     "moe_grouped_fc1_wgrad": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64, _vp,
                                              _vp]),
+    "moe_grouped_fc2_wgrad_accum": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64,
+                                                   _vp, _vp]),
+    "moe_grouped_fc1_wgrad_accum": (ctypes.c_int, [_vp, _vp, _vp, _i64, _i32, _i32, _i32, _i64,
+                                                   _vp, _vp]),
     "moe_route_bwd": (ctypes.c_int, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _i64, _vp, _vp]),
     "moe_probe_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _vp]),
     "moe_probe_write": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp]),
@@ -545,6 +549,33 @@ def moe_grouped_fc1_wgrad(d_preact, x, sorted_slot_ids, E: int, C: int, dw1, str
         _ptr(d_preact, torch.bfloat16, R * 2 * I, "d_preact"), _ptr(x, torch.bfloat16, N * H, "x"),
         _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"), N, H, I, E, C,
         _ptr(dw1, torch.bfloat16, E * 2 * I * H, "dw1"), _stream(stream)))
+
+
+def moe_grouped_fc2_wgrad_accum(dy, act, sorted_slot_ids, E: int, C: int, main_dw2, stream=None):
+    """main_dw2 (float32 [E, H, I]) += the FC2 weight gradient."""
+    N, H = dy.shape
+    R, I = act.shape
+    if R < E * moe_padded_capacity(C):
+        raise ValueError("act must hold E*Cp rows")
+    R = E * moe_padded_capacity(C)
+    _check("moe_grouped_fc2_wgrad_accum", lib.moe_grouped_fc2_wgrad_accum(
+        _ptr(dy, torch.bfloat16, N * H, "dy"), _ptr(act, torch.bfloat16, R * I, "act"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"), N, H, I, E, C,
+        _ptr(main_dw2, torch.float32, E * H * I, "main_dw2"), _stream(stream)))
+
+
+def moe_grouped_fc1_wgrad_accum(d_preact, x, sorted_slot_ids, E: int, C: int, main_dw1, stream=None):
+    """main_dw1 (float32 [E, 2I, H]) += the FC1 weight gradient."""
+    N, H = x.shape
+    R2, I2 = d_preact.shape
+    I = I2 // 2
+    R = E * moe_padded_capacity(C)
+    if R2 < R:
+        raise ValueError("d_preact must hold E*Cp rows")
+    _check("moe_grouped_fc1_wgrad_accum", lib.moe_grouped_fc1_wgrad_accum(
+        _ptr(d_preact, torch.bfloat16, R * 2 * I, "d_preact"), _ptr(x, torch.bfloat16, N * H, "x"),
+        _ptr(sorted_slot_ids, torch.int32, R, "sorted_slot_ids"), N, H, I, E, C,
+        _ptr(main_dw1, torch.float32, E * 2 * I * H, "main_dw1"), _stream(stream)))
 
 
 def moe_route_bwd(topk_ids, topk_probs, token_routes, d_prob, d_logits, stream=None):

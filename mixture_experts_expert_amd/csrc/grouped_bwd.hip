@@ -8,7 +8,9 @@
 //              by the contention-free gather-combine (combine.hip);
 //   section 5  dgrad contracts against the transposed-weight view; wgrad is
 //              expert-centric, contracts over the slot axis with an LDS fill
-//              and transpose reads, and each dW tile has exactly one owner.
+//              and transpose reads, and each dW tile has exactly one owner,
+//              which writes it as bf16 or adds it into a float32 main
+//              gradient inside the kernel.
 //
 // Per expert e (slots [e*Cp, (e+1)*Cp)):
 //
@@ -68,6 +70,7 @@ struct BwdArgs {
     int MT, NT, tiles;
     int64_t b_estride;            // weights: elements between experts (dgrad)
     int64_t o_estride;            // dW: elements between experts (wgrad)
+    float* out32;                 // float32 main gradient the wgrad adds into (or null)
 };
 
 typedef const __attribute__((address_space(4))) int* const_int_ptr;
@@ -290,12 +293,19 @@ __global__ __launch_bounds__(WM * WN * kWave) void dgrad_kernel(BwdArgs p) {
 //     and compute.  Both kinds meet at one barrier per K step: after it the
 //     step's slab is in LDS (the producers waited for it) and the stage
 //     computed at the previous step is free;
-//   * the output goes out in whole 128-byte lines, marked non-temporal: a
-//     consumer stages each 32-row block of its piece in LDS and 8 lanes then
-//     write one row's 128 bytes (stored straight from the accumulator layout,
-//     one instruction would write 32-byte quarters of 32 lines; streamed
-//     partial lines are far slower than whole ones).
-template <int ASRC, int BSRC>
+//   * the bf16 output goes out in whole 128-byte lines, marked non-temporal:
+//     a consumer stages each 32-row block of its piece in LDS and 8 lanes
+//     then write one row's 128 bytes (stored straight from the accumulator
+//     layout, one instruction would write 32-byte quarters of 32 lines;
+//     streamed partial lines are far slower than whole ones);
+//   * ACC32: the tile is added into the float32 main gradient out32 instead
+//     ([PF] section 5, in-kernel main-gradient accumulation): each lane reads
+//     its 4 consecutive columns of a row (16 bytes), adds its float32 sums
+//     and writes them back, default cache policy, so the four quarters of a
+//     128-byte line that neighbouring instructions touch meet in L2.  The
+//     tile's one owner reads and writes every element once: no atomics, and
+//     the result does not depend on the schedule.
+template <int ASRC, int BSRC, bool ACC32 = false>
 __global__ __launch_bounds__(768) void wgrad_kernel(BwdArgs p) {
     constexpr int BMT = 256, BNT = 256, WM = 2, WN = 4, BK = 64, D = 2;
     constexpr int NC = WM * WN;                    // consumer waves
@@ -462,6 +472,35 @@ __global__ __launch_bounds__(768) void wgrad_kernel(BwdArgs p) {
             const int nt = tc % p.NT, rest = tc / p.NT;
             const int e = rest / p.MT;
             const int row0 = (rest % p.MT) * BMT + wm * WTM, col0 = nt * BNT + wn * WTN;
+            if constexpr (ACC32) {
+                const __amdgpu_buffer_rsrc_t mrsrc = __builtin_amdgcn_make_buffer_rsrc(
+                    p.out32 + static_cast<int64_t>(e) * p.o_estride, static_cast<short>(0), p.M * p.ldo * 4,
+                    kRsrcWord3);
+                const int orow = row0 + (lane & 31);
+#pragma unroll
+                for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                    for (int ni = 0; ni < NI; ++ni) {
+                        uint32_t off[4];
+                        u32x4 old[4];
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            const int r = orow + mi * 32, col = col0 + ni * 32 + 8 * g + 4 * half;
+                            off[g] = r < p.M && col < p.Nn ? (static_cast<uint32_t>(r) * p.ldo + col) * 4u : kOob;
+                            old[g] = __builtin_amdgcn_raw_buffer_load_b128(mrsrc, off[g], 0, 0);
+                        }
+#pragma unroll
+                        for (int g = 0; g < 4; ++g) {
+                            u32x4 v;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                v[j] = __float_as_uint(__uint_as_float(old[g][j]) + acc[mi][ni][4 * g + j]);
+                            __builtin_amdgcn_raw_buffer_store_b128(v, mrsrc, off[g], 0, 0);
+                        }
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) acc[mi][ni][j] = 0.0f;
+                    }
+            } else {
             const __amdgpu_buffer_rsrc_t orsrc = __builtin_amdgcn_make_buffer_rsrc(
                 p.out + static_cast<int64_t>(e) * p.o_estride, static_cast<short>(0), p.M * p.ldo * 2, kRsrcWord3);
             // Each 32-row block goes through this wave's LDS block (16-byte
@@ -507,6 +546,7 @@ __global__ __launch_bounds__(768) void wgrad_kernel(BwdArgs p) {
                 }
                 asm volatile("" ::: "memory");
             }
+            }
             ktc = 0;
             tc += G;
         }
@@ -547,7 +587,7 @@ int launch_fc1_dgrad(const BwdArgs& a, int E, hipStream_t s) {
     return MOE_OK;
 }
 
-template <int ASRC, int BSRC>
+template <int ASRC, int BSRC, bool ACC32 = false>
 int launch_wgrad(BwdArgs a, int E, hipStream_t s) {
     constexpr int BT = 256;                        // square output tiles
     a.MT = (a.M + BT - 1) / BT;
@@ -556,7 +596,7 @@ int launch_wgrad(BwdArgs a, int E, hipStream_t s) {
     if (tiles > INT32_MAX) return MOE_ERR_UNSUPPORTED;
     a.tiles = static_cast<int>(tiles);
     // one workgroup (8 consumer + 4 producer waves, all of LDS) per CU
-    wgrad_kernel<ASRC, BSRC><<<std::min(a.tiles, device_cus()), 12 * kWave, 0, s>>>(a);
+    wgrad_kernel<ASRC, BSRC, ACC32><<<std::min(a.tiles, device_cus()), 12 * kWave, 0, s>>>(a);
     return MOE_OK;
 }
 
@@ -664,5 +704,61 @@ extern "C" int moe_grouped_fc1_wgrad(const uint16_t* d_preact, const uint16_t* x
     a.M = 2 * I; a.Nn = H; a.Kd = Cp; a.Cp = Cp;
     a.o_estride = static_cast<int64_t>(2) * I * H;
     st = launch_wgrad<kRowRoute, kRowGather>(a, E, stream);
+    return st != MOE_OK ? st : launch_status();
+}
+
+// Float32 main-gradient forms: the same tiles, K order and float32 sums as
+// the bf16 entry points above, added into main_dw (see ACC32).
+namespace moe {
+namespace {
+
+int check_main(int32_t H, int32_t I) {
+    // one expert's float32 dW must lie within a buffer descriptor's 2 GiB
+    const int64_t big = static_cast<int64_t>(1) << 31;
+    return static_cast<int64_t>(2) * I * H * 4 >= big ? MOE_ERR_UNSUPPORTED : MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" int moe_grouped_fc2_wgrad_accum(const uint16_t* dy, const uint16_t* act,
+                                           const int32_t* sorted_slot_ids, int64_t N, int32_t H,
+                                           int32_t I, int32_t E, int64_t C, float* main_dw2,
+                                           hipStream_t stream) {
+    using namespace moe;
+    int Cp = 0;
+    int st = check_bwd(N, H, I, E, C, &Cp);
+    if (st == MOE_OK) st = check_main(H, I);
+    if (st != MOE_OK) return st;
+    if (N == 0 || C == 0) return MOE_OK;   // nothing routed: the sums are zero
+    st = check_ptrs16({dy, act, sorted_slot_ids, main_dw2});
+    if (st != MOE_OK) return st;
+    BwdArgs a{};
+    a.a = dy; a.b = act; a.sorted_slot_ids = sorted_slot_ids; a.out32 = main_dw2;
+    a.lda = H; a.ldb = I; a.ldo = I; a.N = static_cast<int>(N);
+    a.M = H; a.Nn = I; a.Kd = Cp; a.Cp = Cp;
+    a.o_estride = static_cast<int64_t>(H) * I;
+    st = launch_wgrad<kRowGather, kRowRoute, true>(a, E, stream);
+    return st != MOE_OK ? st : launch_status();
+}
+
+extern "C" int moe_grouped_fc1_wgrad_accum(const uint16_t* d_preact, const uint16_t* x,
+                                           const int32_t* sorted_slot_ids, int64_t N, int32_t H,
+                                           int32_t I, int32_t E, int64_t C, float* main_dw1,
+                                           hipStream_t stream) {
+    using namespace moe;
+    int Cp = 0;
+    int st = check_bwd(N, H, I, E, C, &Cp);
+    if (st == MOE_OK) st = check_main(H, I);
+    if (st != MOE_OK) return st;
+    if (N == 0 || C == 0) return MOE_OK;
+    st = check_ptrs16({d_preact, x, sorted_slot_ids, main_dw1});
+    if (st != MOE_OK) return st;
+    BwdArgs a{};
+    a.a = d_preact; a.b = x; a.sorted_slot_ids = sorted_slot_ids; a.out32 = main_dw1;
+    a.lda = 2 * I; a.ldb = H; a.ldo = H; a.N = static_cast<int>(N);
+    a.M = 2 * I; a.Nn = H; a.Kd = Cp; a.Cp = Cp;
+    a.o_estride = static_cast<int64_t>(2) * I * H;
+    st = launch_wgrad<kRowRoute, kRowGather, true>(a, E, stream);
     return st != MOE_OK ? st : launch_status();
 }

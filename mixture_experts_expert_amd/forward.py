@@ -87,9 +87,14 @@ class MoEBackwardBuffers:
         combine; then backward(dy): FC2 dgrad -> SwiGLU recompute + backward
         -> FC1 dgrad -> gather-combine (dx) -> both weight gradients ->
         router-logit gradient.
+
+    main_grad=True: the weight gradients are added into float32 main
+    gradients main_dw1 / main_dw2 (gradient accumulation over micro-batches;
+    zeroed here, never reset by backward) instead of being written as bf16
+    dw1 / dw2.
     """
 
-    def __init__(self, fwd: MoEBuffers):
+    def __init__(self, fwd: MoEBuffers, main_grad: bool = False):
         self.f = fwd
         R, N, H, I, E = fwd.R, fwd.N, fwd.H, fwd.I, fwd.E
         dev = fwd.act.device
@@ -105,8 +110,13 @@ class MoEBackwardBuffers:
         self.d_prob = z((R,), f32)
         self.d_a = z((R, H), bf16)
         self.dx = z((N, H), bf16)
-        self.dw1 = z((E, 2 * I, H), bf16)
-        self.dw2 = z((E, H, I), bf16)
+        self.main_grad = bool(main_grad)
+        if self.main_grad:
+            self.main_dw1 = z((E, 2 * I, H), f32)
+            self.main_dw2 = z((E, H, I), f32)
+        else:
+            self.dw1 = z((E, 2 * I, H), bf16)
+            self.dw2 = z((E, H, I), bf16)
         self.d_logits = z((N, E), f32)
 
     def fc1_swiglu_save(self, x, w1, stream=None):
@@ -137,12 +147,20 @@ class MoEBackwardBuffers:
         nat.moe_gather_combine(self.d_a, self.f.token_routes, self.dx, stream)
 
     def fc2_wgrad(self, dy, stream=None):
-        nat.moe_grouped_fc2_wgrad(dy, self.act_re, self.f.sorted_slot_ids, self.f.E, self.f.C,
-                                  self.dw2, stream)
+        if self.main_grad:
+            nat.moe_grouped_fc2_wgrad_accum(dy, self.act_re, self.f.sorted_slot_ids, self.f.E,
+                                            self.f.C, self.main_dw2, stream)
+        else:
+            nat.moe_grouped_fc2_wgrad(dy, self.act_re, self.f.sorted_slot_ids, self.f.E, self.f.C,
+                                      self.dw2, stream)
 
     def fc1_wgrad(self, x, stream=None):
-        nat.moe_grouped_fc1_wgrad(self.d_preact, x, self.f.sorted_slot_ids, self.f.E, self.f.C,
-                                  self.dw1, stream)
+        if self.main_grad:
+            nat.moe_grouped_fc1_wgrad_accum(self.d_preact, x, self.f.sorted_slot_ids, self.f.E,
+                                            self.f.C, self.main_dw1, stream)
+        else:
+            nat.moe_grouped_fc1_wgrad(self.d_preact, x, self.f.sorted_slot_ids, self.f.E, self.f.C,
+                                      self.dw1, stream)
 
     def route_bwd(self, stream=None):
         f = self.f
@@ -150,7 +168,8 @@ class MoEBackwardBuffers:
                           stream)
 
     def backward(self, dy, x, w1, w2, stream=None):
-        """All backward steps in order; results in dx, dw1, dw2, d_logits."""
+        """All backward steps in order; results in dx, dw1, dw2 (or added into
+        main_dw1, main_dw2), d_logits."""
         self.fc2_dgrad(dy, w2, stream)
         self.swiglu_bwd(stream)
         self.fc1_dgrad(w1, stream)

@@ -26,6 +26,7 @@ def test_every_declared_symbol_is_exported():
                           "moe_gather_combine", "moe_grouped_fc1_swiglu_save",
                           "moe_grouped_fc2_dgrad", "moe_swiglu_bwd", "moe_grouped_fc1_dgrad",
                           "moe_grouped_fc2_wgrad", "moe_grouped_fc1_wgrad", "moe_route_bwd",
+                          "moe_grouped_fc2_wgrad_accum", "moe_grouped_fc1_wgrad_accum",
                           "moe_route_dropless_live", "moe_dispatch_rows",
                           "moe_grouped_fc2_rows", "moe_route_capacity_workspace_bytes",
                           "moe_route_capacity_align_noalloc"}
@@ -268,12 +269,18 @@ def test_backward_validation():
     assert f(A, A, A, A, 16, 64, 64, 4, 8, A, MIS, NUL) == MISALIGNED
     assert f(A, A, A, A, 16, 64, 64, 4, 8, A, NUL, NUL) == INVALID
     assert f(*([NUL] * 4), 0, 64, 64, 4, 0, NUL, NUL, NUL) == OK
-    for g in (lib.moe_grouped_fc2_dgrad, lib.moe_grouped_fc2_wgrad, lib.moe_grouped_fc1_wgrad):
+    for g in (lib.moe_grouped_fc2_dgrad, lib.moe_grouped_fc2_wgrad, lib.moe_grouped_fc1_wgrad,
+              lib.moe_grouped_fc2_wgrad_accum, lib.moe_grouped_fc1_wgrad_accum):
         assert g(A, A, A, 16, 64, 96, 4, 8, A, NUL) == UNSUPPORTED                   # I % 64
         assert g(A, A, A, -1, 64, 64, 4, 8, A, NUL) == INVALID                        # N < 0
         assert g(A, A, NUL, 16, 64, 64, 4, 8, A, NUL) == INVALID
         assert g(A, A, A, 16, 64, 64, 4, 8, MIS, NUL) == MISALIGNED
         assert g(NUL, NUL, NUL, 0, 64, 64, 4, 0, NUL, NUL) == OK
+    for g in (lib.moe_grouped_fc2_wgrad_accum, lib.moe_grouped_fc1_wgrad_accum):
+        # one expert's float32 gradient (2*I*H*4 bytes) reaches 2 GiB; its bf16 one does not
+        assert g(A, A, A, 16, 16384, 16384, 4, 8, A, NUL) == UNSUPPORTED
+        assert g(A, A, A, 16, 16384, 8192, 4, 8, NUL, NUL) == INVALID
+    assert lib.moe_grouped_fc1_wgrad(A, A, A, 16, 16384, 16384, 4, 8, NUL, NUL) == INVALID
     g = lib.moe_grouped_fc1_dgrad
     assert g(A, A, 16, 64, 64, 2048, 8, A, NUL) == UNSUPPORTED                         # E > 1024
     assert g(A, NUL, 16, 64, 64, 4, 8, A, NUL) == INVALID

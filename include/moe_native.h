@@ -380,7 +380,8 @@ int moe_dispatch_rows(const uint16_t* x, const int32_t* sorted_slot_ids, int64_t
  * row(s) = sorted_slot_ids[s]; pad slots (row N) contribute nothing.  All
  * bf16 results are rounded once (nearest-even) from float32 accumulators.
  * The sizes and envelope are the forward's (N, H, I, E, C as there, R = E*Cp);
- * outputs are fully overwritten (dW included: no accumulation into them),
+ * outputs are fully overwritten (dW included; the _accum forms below add
+ * into float32 main gradients instead),
  * except that N == 0 or C == 0 is a no-op that leaves every output as it was.
  * ------------------------------------------------------------------------ */
 

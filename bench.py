@@ -279,6 +279,57 @@ def access_order_probes(torch, moe, w, reps=10):
     print(json.dumps(out))
 
 
+def gemm_loop_probe(torch, moe, w, reps=10):
+    """The grouped GEMMs' K loop alone (the library's GEMM-loop probe: same
+    tiles, rings and MFMA, no gather, no epilogue) at the workload's FC1 and
+    FC2 shapes, with seeded random bf16 operands, beside the layer's own FC1
+    and FC2 timed the same way in the same process.  Prints one JSON line."""
+    Cp = moe.moe_padded_capacity(moe.moe_source_capacity(w.N, w.K, w.E, w.F))
+    Cp = (Cp + 255) // 256 * 256                          # whole 256-row tiles
+    shapes = {"fc1": (2 * w.I, w.H), "fc2": (w.H, w.I)}   # (N, K) of each product
+    out = {"probe": "gemm_loop", "workload": w.name, "E": w.E, "Cp": Cp, "reps": reps, "shapes": {}}
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.Stream()
+    g = torch.Generator(device="cuda").manual_seed(5)
+    for name, (Nn, Kd) in shapes.items():
+        a = torch.randn(w.E * Cp, Kd, generator=g, device="cuda").to(torch.bfloat16)
+        b = (torch.randn(w.E, Nn, Kd, generator=g, device="cuda") * 0.02).to(torch.bfloat16)
+        flops = 2.0 * w.E * Cp * Nn * Kd
+        with torch.cuda.stream(stream):
+            warm(lambda: moe.moe_probe_gemm_loop(a, b, w.E, Cp, sink, stream), 3, 0.5, stream)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(reps):
+                moe.moe_probe_gemm_loop(a, b, w.E, Cp, sink, stream)
+            ev[1].record(stream)
+            stream.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+        out["shapes"][name] = {"N": Nn, "K": Kd, "gflop": flops / 1e9, "loop_us": us,
+                               "loop_tflops": flops / (us * 1e-6) / 1e12}
+        del a, b
+    # the layer's own FC1 and FC2 on the workload's inputs, in the same process
+    import moe_inputs
+    T = moe_inputs.make_tensors(w, "cuda")
+    buf = moe.MoEBuffers(w.N, w.H, w.I, w.E, w.K, w.F, "cuda")
+    buf.route_capacity_align(T["logits"])
+    for name, fn in (("fc1", lambda: buf.fc1_swiglu(T["x"], T["w1"], stream)),
+                     ("fc2", lambda: buf.fc2(T["w2"], stream))):
+        with torch.cuda.stream(stream):
+            warm(fn, 3, 0.5, stream)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(stream)
+            for _ in range(reps):
+                fn()
+            ev[1].record(stream)
+            stream.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3 / reps
+        rec = out["shapes"][name]
+        rec["kernel_us"] = us
+        rec["kernel_tflops"] = rec["gflop"] * 1e9 / (us * 1e-6) / 1e12
+    log("[bench] gemm-loop probe: " + json.dumps(out["shapes"]))
+    print(json.dumps(out))
+
+
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
     """A plain device copy of known size, for scaling the FETCH/WRITE counters."""
     src = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
@@ -803,6 +854,10 @@ def main():
     ap.add_argument("--access-order-probes", action="store_true",
                     help="only time the library's access-order and LDS-ring probes over a buffer "
                          "the size of the workload's W1, print one JSON line and exit")
+    ap.add_argument("--gemm-loop-probe", action="store_true",
+                    help="only time the library's GEMM-loop probe (the grouped GEMMs' K loop with no "
+                         "gather and no epilogue) at the workload's FC1 and FC2 shapes, print one JSON "
+                         "line and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -821,6 +876,9 @@ def main():
     w = moe_inputs.WORKLOADS[args.workload or moe_inputs.HEADLINE]
     if args.access_order_probes:
         access_order_probes(torch, moe, w)
+        return
+    if args.gemm_loop_probe:
+        gemm_loop_probe(torch, moe, w)
         return
     if args.vendor_reference:
         vendor_reference(torch, moe, w, args)

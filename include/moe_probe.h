@@ -6,7 +6,9 @@
  * layer's kernels against those rates (the published 8 TB/s is a nominal
  * peak no access pattern reaches); the access-order probes state what the
  * order of a GEMM tile's weight reads and output writes, and the LDS-DMA
- * ring the GEMMs load through, cost by themselves.
+ * ring the GEMMs load through, cost by themselves; the GEMM-loop probe
+ * (libmoe_native's gemm_probe.hip) runs the GEMMs' K loop with no gather
+ * and no epilogue.
  *
  * Conventions: device pointers owned by the caller, 16-byte aligned, byte
  * counts multiples of 16 (MOE_ERR_MISALIGNED otherwise); a null pointer is
@@ -75,6 +77,19 @@ int moe_probe_write_tiles(void* dst, size_t bytes, int32_t row_bytes, int32_t ro
  * writes at most one word to sink[0]. */
 int moe_probe_lds_ring(const void* src, size_t bytes, int32_t stages, uint32_t* sink,
                        hipStream_t stream);
+
+/* The grouped FFN GEMMs' K loop alone: E experts' products
+ * a[e*Cp .. e*Cp+Cp) (rows of K bf16) times b[e] ([N][K] bf16) over the same
+ * 256x256 tiles, 64-deep slabs, LDS-DMA rings (two A and three B stages),
+ * persistent XCD-aware tile walk and bf16 MFMA as the layer's kernels, with no
+ * gather, no epilogue and no output: each finished tile folds into a word
+ * written to sink[0] only in a case that does not occur.  Eight waves of
+ * 128x64 outputs each, as the layer's kernels.  Device pointers, a and b
+ * 16-byte aligned (MOE_ERR_MISALIGNED); null pointers or negative sizes are
+ * MOE_ERR_INVALID_ARG; Cp and N multiples of 256 and K of 64, one expert's a
+ * rows and b below 2 GiB (MOE_ERR_UNSUPPORTED); any size 0 is a no-op. */
+int moe_probe_gemm_loop(const uint16_t* a, const uint16_t* b, int32_t E, int32_t Cp, int32_t N,
+                        int32_t K, uint32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -32,6 +32,7 @@ from ._native import (  # noqa: F401
     moe_layout_block_m,
     moe_padded_capacity,
     moe_probe_copy,
+    moe_probe_gemm_loop,
     moe_probe_lds_ring,
     moe_probe_read,
     moe_probe_read_pieces,

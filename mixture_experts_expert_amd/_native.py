@@ -85,6 +85,7 @@ _SIGNATURES = {
     "moe_probe_read_pieces": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _i32, _vp, _vp]),
     "moe_probe_write_pieces": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _i32, _i32, _vp]),
     "moe_probe_write_tiles": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _i32, _i32, _vp]),
+    "moe_probe_gemm_loop": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "moe_probe_lds_ring": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
@@ -151,6 +152,18 @@ def moe_probe_write_tiles(dst, row_bytes: int, rows: int, piece_bytes: int, nont
     p, n = _bytes_ptr(dst, "dst")
     _check("moe_probe_write_tiles", lib.moe_probe_write_tiles(
         p, n, row_bytes, rows, piece_bytes, int(bool(nontemporal)), _stream(stream)))
+
+
+def moe_probe_gemm_loop(a, b, E: int, Cp: int, sink, stream=None):
+    """The grouped GEMMs' K loop alone over E experts: a bf16 [E*Cp, K],
+    b bf16 [E, N, K] (an access-order-style probe); sink: int32 device tensor."""
+    K = a.shape[-1]
+    N = b.shape[-2]
+    if b.shape[-1] != K or a.numel() < E * Cp * K or b.numel() < E * N * K:
+        raise ValueError("moe_probe_gemm_loop: a must be [E*Cp, K] and b [E, N, K]")
+    _check("moe_probe_gemm_loop", lib.moe_probe_gemm_loop(
+        _ptr(a, torch.bfloat16, E * Cp * K, "a"), _ptr(b, torch.bfloat16, E * N * K, "b"), E, Cp, N, K,
+        _bytes_ptr(sink, "sink")[0], _stream(stream)))
 
 
 def moe_probe_lds_ring(src, stages: int, sink, stream=None):

@@ -38,7 +38,7 @@ def test_probe_header_symbols_and_validation():
     names = moe.header_functions(moe.PROBE_HEADER_PATH)
     assert set(names) == {"moe_probe_read", "moe_probe_write", "moe_probe_copy",
                           "moe_probe_read_pieces", "moe_probe_write_pieces", "moe_probe_write_tiles",
-                          "moe_probe_lds_ring"}
+                          "moe_probe_lds_ring", "moe_probe_gemm_loop"}
     for n in names:
         assert hasattr(lib, n), n
     big = ctypes.c_size_t(1 << 20)
@@ -74,6 +74,15 @@ def test_probe_header_symbols_and_validation():
     assert lib.moe_probe_lds_ring(ALIGNED, ctypes.c_size_t(4096), 3, ALIGNED, NUL) == INVALID
     assert lib.moe_probe_lds_ring(ALIGNED, big, 3, NUL, NUL) == INVALID
     assert lib.moe_probe_lds_ring(ALIGNED, ctypes.c_size_t(0), 3, ALIGNED, NUL) == OK
+    g = lib.moe_probe_gemm_loop
+    assert g(NUL, ALIGNED, 4, 256, 256, 128, ALIGNED, NUL) == INVALID
+    assert g(ALIGNED, ALIGNED, 4, 256, 256, 128, NUL, NUL) == INVALID
+    assert g(MIS, ALIGNED, 4, 256, 256, 128, ALIGNED, NUL) == MISALIGNED
+    assert g(ALIGNED, ALIGNED, -1, 256, 256, 128, ALIGNED, NUL) == INVALID
+    assert g(ALIGNED, ALIGNED, 4, 200, 256, 128, ALIGNED, NUL) == UNSUPPORTED   # Cp % 256
+    assert g(ALIGNED, ALIGNED, 4, 256, 256, 100, ALIGNED, NUL) == UNSUPPORTED   # K % 64
+    assert g(ALIGNED, ALIGNED, 4, 256, 1 << 20, 1 << 10, ALIGNED, NUL) == UNSUPPORTED   # 2 GiB
+    assert g(ALIGNED, ALIGNED, 0, 256, 256, 128, ALIGNED, NUL) == OK
 
 
 def test_capacity_golden_values():

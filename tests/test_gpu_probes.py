@@ -66,3 +66,14 @@ def test_lds_ring_runs(stages):
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     moe.moe_probe_lds_ring(src, stages, sink)
     torch.cuda.synchronize()
+
+
+def test_gemm_loop_runs():
+    """The GEMM-loop probe runs over several tiles per workgroup and experts
+    (two row tiles, ragged tile count against the CUs)."""
+    E, Cp, N, K = 3, 512, 768, 192
+    a = torch.randn(E * Cp, K, device="cuda").to(torch.bfloat16)
+    b = torch.randn(E, N, K, device="cuda").to(torch.bfloat16)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    moe.moe_probe_gemm_loop(a, b, E, Cp, sink)
+    torch.cuda.synchronize()

@@ -226,6 +226,43 @@ def hbm_probes(torch, moe, stream, nbytes=2 << 30, reps=10):
     return out
 
 
+def compute_probes(torch, moe, stream, reps=5):
+    """What a compute unit's matrix cores and LDS reach with nothing else in
+    the way (the library's matrix-core and LDS-read probes, one workgroup per
+    compute unit): the bf16 MFMA rate and the engine clock it runs at, and
+    the LDS read bytes per engine clock per compute unit.  The matrix-core
+    rate is the attainable one on this device: under full MFMA load the
+    engine clock drops below the 2.4 GHz the published peak assumes."""
+    groups = torch.cuda.get_device_properties(0).multi_processor_count
+    clocks = torch.zeros(2 * groups, dtype=torch.int64, device="cuda")
+    out = {}
+    with torch.cuda.stream(stream):
+        for name, fn, iters in (("mfma", moe.moe_probe_mfma_rate, 10000), ("lds", moe.moe_probe_lds_read, 10000)):
+            for _ in range(2):
+                fn(groups, iters, clocks, stream)
+            ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ev0.record(stream)
+            for _ in range(reps):
+                fn(groups, iters, clocks, stream)
+            ev1.record(stream)
+            stream.synchronize()
+            sec = ev0.elapsed_time(ev1) * 1e-3 / reps
+            c = clocks.view(groups, 2).double().cpu()
+            ghz = float((c[:, 0] / c[:, 1]).median()) * 0.1
+            if name == "mfma":
+                flops = groups * 8 * 4 * iters * 32768.0
+                out["mfma_tflops"] = flops / sec / 1e12
+                out["mfma_frac_bf16_peak"] = out["mfma_tflops"] / PEAK_BF16_TFLOPS
+                out["mfma_clock_ghz"] = ghz
+            else:
+                per_wg = 8 * 8 * 1024.0 * iters
+                out["lds_read_bytes_per_clock_per_cu"] = per_wg / float(c[:, 0].median())
+                out["lds_read_tbs"] = groups * per_wg / sec / 1e12
+                out["lds_clock_ghz"] = ghz
+    log("[bench] compute probes: " + ", ".join(f"{k} {v:.3f}" for k, v in out.items()))
+    return out
+
+
 def access_order_probes(torch, moe, w, reps=10):
     """GB/s of the library's access-order probes over a buffer the size of
     the workload's W1 ([E, 2I, H] bf16, as panels of 256 rows of H*2 bytes):
@@ -920,6 +957,7 @@ def main():
     ms_per_step = time_graph(torch, fwd, stream, args, replay)
     us = time_calls(torch, names, calls, stream, args)
     probes = hbm_probes(torch, moe, stream)
+    cprobes = compute_probes(torch, moe, stream)
 
     kept = int((buf.token_routes >= 0).sum().item())
     if dropless:
@@ -959,6 +997,10 @@ def main():
         "gemm_frac_bf16_peak": gemm_tflops / PEAK_BF16_TFLOPS,
         # the same GEMM time credited only with the kept routes' work
         "useful_tflops": 6.0 * w.H * w.I * kept / ((us["fc1"] + us["fc2"]) * 1e-6) / 1e12,
+        # the matrix cores' attainable rate on this device (a probe issuing
+        # nothing but MFMAs) and the LDS read rate, with their engine clocks
+        "compute_probe": cprobes,
+        "gemm_frac_mfma_probe": gemm_tflops / cprobes["mfma_tflops"],
         "kernel_us": us,
         "kernel_gbs": gbs,
         "kernel_frac_hbm_peak": {n: gbs[n] / PEAK_HBM_GBS for n in names},

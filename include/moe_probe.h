@@ -8,7 +8,9 @@
  * order of a GEMM tile's weight reads and output writes, and the LDS-DMA
  * ring the GEMMs load through, cost by themselves; the GEMM-loop probe
  * (libmoe_native's gemm_probe.hip) runs the GEMMs' K loop with no gather
- * and no epilogue.
+ * and no epilogue; the matrix-core and LDS-read probes state the bf16 MFMA
+ * rate and the LDS read rate a compute unit reaches with nothing else in
+ * the way, and the engine clock it runs them at.
  *
  * Conventions: device pointers owned by the caller, 16-byte aligned, byte
  * counts multiples of 16 (MOE_ERR_MISALIGNED otherwise); a null pointer is
@@ -90,6 +92,21 @@ int moe_probe_lds_ring(const void* src, size_t bytes, int32_t stages, uint32_t* 
  * rows and b below 2 GiB (MOE_ERR_UNSUPPORTED); any size 0 is a no-op. */
 int moe_probe_gemm_loop(const uint16_t* a, const uint16_t* b, int32_t E, int32_t Cp, int32_t N,
                         int32_t K, uint32_t* sink, hipStream_t stream);
+
+/* The matrix cores alone: `groups` workgroups of 512 threads (one per
+ * compute unit: each holds 96 KB of LDS; pass at most the device's compute
+ * unit count), every wave issuing `iters` x 4 bf16 32x32x16 MFMAs on four
+ * independent accumulators (32768 flops each) and nothing else.  The LDS read
+ * path alone: the same workgroups, every wave issuing `iters` x 8 16-byte
+ * LDS reads per lane (1 KB per wave and read, eight in flight, no bank
+ * conflicts, no ALU work).  Each workgroup g writes clocks[2g] = engine-clock
+ * ticks (s_memtime) and clocks[2g + 1] = 100 MHz constant-clock ticks
+ * (s_memrealtime) over its loop, bracketed by workgroup barriers, so
+ * 1e8 * clocks[2g] / clocks[2g + 1] is the engine clock in Hz.  clocks is a
+ * device buffer of 2 * groups words, 8-byte aligned.  A null clocks,
+ * groups < 0 or iters < 1 is MOE_ERR_INVALID_ARG; groups == 0 is a no-op. */
+int moe_probe_mfma_rate(int32_t groups, int32_t iters, uint64_t* clocks, hipStream_t stream);
+int moe_probe_lds_read(int32_t groups, int32_t iters, uint64_t* clocks, hipStream_t stream);
 
 #ifdef __cplusplus
 }

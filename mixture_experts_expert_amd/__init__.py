@@ -33,7 +33,9 @@ from ._native import (  # noqa: F401
     moe_padded_capacity,
     moe_probe_copy,
     moe_probe_gemm_loop,
+    moe_probe_lds_read,
     moe_probe_lds_ring,
+    moe_probe_mfma_rate,
     moe_probe_read,
     moe_probe_read_pieces,
     moe_probe_write,

@@ -87,6 +87,8 @@ _SIGNATURES = {
     "moe_probe_write_tiles": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _i32, _i32, _i32, _vp]),
     "moe_probe_gemm_loop": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp]),
     "moe_probe_lds_ring": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _vp, _vp]),
+    "moe_probe_mfma_rate": (ctypes.c_int, [_i32, _i32, _vp, _vp]),
+    "moe_probe_lds_read": (ctypes.c_int, [_i32, _i32, _vp, _vp]),
 }
 for _name, (_res, _args) in _SIGNATURES.items():
     _fn = getattr(lib, _name)
@@ -172,6 +174,29 @@ def moe_probe_lds_ring(src, stages: int, sink, stream=None):
     p, n = _bytes_ptr(src, "src")
     _check("moe_probe_lds_ring", lib.moe_probe_lds_ring(p, n, stages, _bytes_ptr(sink, "sink")[0],
                                                         _stream(stream)))
+
+
+def _clocks(clocks, groups: int, fn: str):
+    if (not isinstance(clocks, torch.Tensor) or not clocks.is_cuda or clocks.dtype != torch.int64
+            or not clocks.is_contiguous() or clocks.numel() < 2 * groups):
+        raise ValueError(f"{fn}: clocks must be a contiguous int64 device tensor of 2 * groups words")
+    return ctypes.c_void_p(clocks.data_ptr())
+
+
+def moe_probe_mfma_rate(groups: int, iters: int, clocks, stream=None):
+    """The matrix cores alone: `groups` workgroups (one per compute unit),
+    each wave issuing iters x 4 bf16 32x32x16 MFMAs; clocks: int64 device
+    tensor of 2 * groups words (engine-clock, constant-clock ticks per
+    workgroup)."""
+    _check("moe_probe_mfma_rate", lib.moe_probe_mfma_rate(
+        groups, iters, _clocks(clocks, groups, "moe_probe_mfma_rate"), _stream(stream)))
+
+
+def moe_probe_lds_read(groups: int, iters: int, clocks, stream=None):
+    """The LDS read path alone: `groups` workgroups (one per compute unit),
+    each wave issuing iters x 8 reads of 1 KB; clocks as moe_probe_mfma_rate."""
+    _check("moe_probe_lds_read", lib.moe_probe_lds_read(
+        groups, iters, _clocks(clocks, groups, "moe_probe_lds_read"), _stream(stream)))
 
 
 class MoEError(RuntimeError):

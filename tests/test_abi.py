@@ -38,7 +38,8 @@ def test_probe_header_symbols_and_validation():
     names = moe.header_functions(moe.PROBE_HEADER_PATH)
     assert set(names) == {"moe_probe_read", "moe_probe_write", "moe_probe_copy",
                           "moe_probe_read_pieces", "moe_probe_write_pieces", "moe_probe_write_tiles",
-                          "moe_probe_lds_ring", "moe_probe_gemm_loop"}
+                          "moe_probe_lds_ring", "moe_probe_gemm_loop", "moe_probe_mfma_rate",
+                          "moe_probe_lds_read"}
     for n in names:
         assert hasattr(lib, n), n
     big = ctypes.c_size_t(1 << 20)
@@ -83,6 +84,11 @@ def test_probe_header_symbols_and_validation():
     assert g(ALIGNED, ALIGNED, 4, 256, 256, 100, ALIGNED, NUL) == UNSUPPORTED   # K % 64
     assert g(ALIGNED, ALIGNED, 4, 256, 1 << 20, 1 << 10, ALIGNED, NUL) == UNSUPPORTED   # 2 GiB
     assert g(ALIGNED, ALIGNED, 0, 256, 256, 128, ALIGNED, NUL) == OK
+    for f in (lib.moe_probe_mfma_rate, lib.moe_probe_lds_read):
+        assert f(256, 100, NUL, NUL) == INVALID       # no clocks buffer
+        assert f(-1, 100, ALIGNED, NUL) == INVALID
+        assert f(256, 0, ALIGNED, NUL) == INVALID     # iters < 1
+        assert f(0, 100, ALIGNED, NUL) == OK          # no workgroups: nothing to do
 
 
 def test_capacity_golden_values():

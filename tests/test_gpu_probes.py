@@ -77,3 +77,28 @@ def test_gemm_loop_runs():
     sink = torch.zeros(4, dtype=torch.int32, device="cuda")
     moe.moe_probe_gemm_loop(a, b, E, Cp, sink)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("probe", ["mfma", "lds"])
+def test_compute_probes_record_their_clocks(probe):
+    """Every workgroup of the matrix-core and LDS-read probes records its
+    engine-clock and constant-clock ticks; the ratio is a clock in the range a
+    GPU engine runs at, and the MFMA probe's issue rate per SIMD stays at or
+    below one 32x32x16 MFMA per 32 engine clocks (a pipe's full rate: 512
+    bf16 multiply-adds per clock)."""
+    groups = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 2000
+    clocks = torch.zeros(2 * groups, dtype=torch.int64, device="cuda")
+    f = moe.moe_probe_mfma_rate if probe == "mfma" else moe.moe_probe_lds_read
+    f(groups, iters, clocks)
+    torch.cuda.synchronize()
+    c = clocks.view(groups, 2).cpu()
+    assert bool((c > 0).all())
+    ghz = c[:, 0].double() / c[:, 1].double() * 0.1
+    assert 0.3 < float(ghz.min()) and float(ghz.max()) < 4.0
+    if probe == "mfma":
+        # each SIMD hosts two of the eight waves: 2 * 4 * iters MFMAs per SIMD
+        ticks_per_mfma = c[:, 0].double() / (2 * 4 * iters)
+        assert float(ticks_per_mfma.min()) >= 32 * 0.97
+    with pytest.raises(ValueError):
+        f(groups, iters, clocks[:-1])

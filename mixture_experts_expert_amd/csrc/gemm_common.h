@@ -23,6 +23,9 @@ constexpr int kRsrcWord3 = 0x00020000;   // raw buffer, 32-bit data format (CDNA
 constexpr uint32_t kOob = 0x80000000u;
 // cache-policy operand of a buffer store: non-temporal (streamed)
 constexpr int kStoreNT = 2;
+// cache-policy operand of a buffer store: scope bits sc0 sc1 (system
+// scope), so the L2 writes the line through instead of keeping it dirty
+constexpr int kStoreSys = 17;
 
 __device__ __forceinline__ int xcd_remap(int bid, int G) {
     const int q = G / kXcds, r = G % kXcds;

@@ -533,7 +533,7 @@ __global__ __launch_bounds__(WM * WN * kWave) void ffn_gemm_kernel(FfnArgs p) {
             return d;
         };
         if constexpr (EPI != 0) {
-            constexpr int POLICY = EPI == 2 ? kStoreNT : 0;
+            constexpr int POLICY = EPI == 2 ? kStoreNT : kStoreSys;
             typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
             __syncthreads();                                // every wave is past the last K step
             const uint32_t rA = static_cast<uint32_t>(a_fill), rB = static_cast<uint32_t>(B_RING + b_fill);
@@ -740,9 +740,12 @@ int launch_gemm(FfnArgs a, bool fc1, int E, hipStream_t s, bool dyn = false) {
     a.E = E;
     // Tiles of 256 x 256 (FC1 and FC2) and 320 x 256 (FC2) leave through the
     // staged epilogue: FC1's activation non-temporal (FC2 reads it from HBM
-    // at no measured cost), FC2's route_out with the default policy (the
-    // combine reads it next, partly from cache).  A 320-row FC1 tile keeps
-    // direct stores: staged, its registers spill (280 vs 233 us).
+    // at no measured cost), FC2's route_out with system scope (written
+    // through the L2, so it does not evict the activation rows the expert's
+    // other column tiles still read; the combine that reads route_out next
+    // runs as fast as after default-policy stores, while non-temporal ones
+    // slow it).  A 320-row FC1 tile keeps direct stores: staged, its
+    // registers spill (280 vs 233 us).
     constexpr bool SHAPE = BNT == 256 && BK == 64 && WM == 2 && WN == 4;
     constexpr bool STAGED = SHAPE && BMT == 256;
     constexpr bool STAGED2 = SHAPE && (BMT == 256 || BMT == 320);

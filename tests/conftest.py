@@ -24,7 +24,13 @@ if _build.is_stale():
     _build.build(verbose=True)
 
 
+@pytest.hookimpl(tryfirst=True)
 def pytest_configure(config):
+    # A test stuck in a device call ends after 600 s with its name, instead
+    # of holding the whole run, unless the command line sets a timeout.
+    if hasattr(config.option, "timeout") and not config.option.timeout:
+        config.option.timeout = 600.0
+        config.option.timeout_method = "thread"
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: full-size workload, minutes on the CPU side")
 
